@@ -1,0 +1,284 @@
+// C-ABI of libmcsparse: argument validation, dispatch to the gfx950 kernels,
+// error reporting. Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "mcs_internal.hpp"
+#include "mcsparse.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mcs_status_t fail(mcs_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mcs_status_t ok() { return MCS_OK; }
+
+mcs_status_t hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return MCS_OK;
+  return fail(MCS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// extent in elements of a [B,N,H,d] tensor under the descriptor's strides
+int64_t extent(const mcs_attn_desc_t *d) {
+  return (int64_t)(d->batch - 1) * d->stride_b + (int64_t)(d->seqlen - 1) * d->stride_n +
+         (int64_t)(d->heads - 1) * d->stride_h + d->head_dim;
+}
+
+bool overlaps(const void *a, const void *b, int64_t bytes) {
+  const char *x = (const char *)a, *y = (const char *)b;
+  return x < y + bytes && y < x + bytes;
+}
+
+mcs_status_t check_desc(const mcs_attn_desc_t *d) {
+  if (!d) return fail(MCS_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->batch < 1 || d->heads < 1 || d->seqlen < 1)
+    return fail(MCS_ERR_INVALID_ARGUMENT, "batch, heads and seqlen must be >= 1 (got %d, %d, %d)",
+                d->batch, d->heads, d->seqlen);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(MCS_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->stride_b < 0 || d->stride_n < 0 || d->stride_h < 0 || d->stride_b % 8 || d->stride_n % 8 ||
+      d->stride_h % 8)
+    return fail(MCS_ERR_INVALID_ARGUMENT, "strides must be non-negative multiples of 8 elements");
+  if ((int64_t)d->batch * d->heads * d->seqlen > ((int64_t)1 << 31) - 1)
+    return fail(MCS_ERR_INVALID_ARGUMENT, "batch*heads*seqlen exceeds 2^31-1");
+  if (!std::isfinite(d->scale)) return fail(MCS_ERR_INVALID_ARGUMENT, "scale is not finite");
+  return ok();
+}
+
+mcs_status_t check_tensor(const void *p, const char *name) {
+  if (!p) return fail(MCS_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MCS_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return ok();
+}
+
+mcs_status_t check_ptr(const void *p, const char *name) {
+  if (!p) return fail(MCS_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (((uintptr_t)p & 3u) != 0) return fail(MCS_ERR_INVALID_ARGUMENT, "%s is not 4-byte aligned", name);
+  return ok();
+}
+
+mcs_status_t check_group(int32_t T) {
+  if (T != 64 && T != 128) return fail(MCS_ERR_UNSUPPORTED, "group_size %d not supported (64 or 128)", T);
+  return ok();
+}
+
+mcs_status_t check_topk(const mcs_attn_desc_t *d, int32_t K) {
+  if (K < 1 || K > d->seqlen) return fail(MCS_ERR_INVALID_ARGUMENT, "topk %d outside [1, %d]", K, d->seqlen);
+  return ok();
+}
+
+#define MCS_TRY(x)                   \
+  do {                               \
+    const mcs_status_t _st = (x);    \
+    if (_st != MCS_OK) return _st;   \
+  } while (0)
+
+mcs::AttnArgs attn_args(const mcs_attn_desc_t *d) {
+  mcs::AttnArgs a{};
+  a.sb = d->stride_b;
+  a.sn = d->stride_n;
+  a.sh = d->stride_h;
+  a.B = d->batch;
+  a.H = d->heads;
+  a.N = d->seqlen;
+  a.scale_log2 = d->scale * 1.4426950408889634f;
+  return a;
+}
+
+int32_t groups_of(const mcs_attn_desc_t *d, int32_t T) { return (d->seqlen + T - 1) / T; }
+
+mcs_status_t check_out_alias(const mcs_attn_desc_t *d, const void *out, const char *oname,
+                             std::initializer_list<std::pair<const void *, const char *>> ins) {
+  const int64_t bytes = extent(d) * 2;
+  for (const auto &in : ins)
+    if (in.first && overlaps(out, in.first, bytes))
+      return fail(MCS_ERR_INVALID_ARGUMENT, "%s overlaps %s", oname, in.second);
+  return ok();
+}
+
+}  // namespace
+
+namespace mcs {
+void set_last_error(const char *msg) { g_last_error = msg; }
+}  // namespace mcs
+
+extern "C" {
+
+int32_t mcs_version(void) { return 100; }
+
+const char *mcs_last_error(void) { return g_last_error.c_str(); }
+
+mcs_status_t mcs_pddp_group_workspace_size(const mcs_attn_desc_t *desc, int32_t group_size,
+                                           size_t *bytes) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_group(group_size));
+  if (!bytes) return fail(MCS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = mcs::pddp_workspace_bytes(desc->batch, desc->heads, desc->seqlen, desc->head_dim, group_size);
+  return ok();
+}
+
+mcs_status_t mcs_pddp_group(const mcs_attn_desc_t *desc, const void *q, int32_t group_size,
+                            int32_t power_iters, int32_t *perm, void *ws, size_t ws_bytes,
+                            mcs_stream_t stream) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_group(group_size));
+  MCS_TRY(check_tensor(q, "q"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  if (power_iters < 1 || power_iters > 64)
+    return fail(MCS_ERR_INVALID_ARGUMENT, "power_iters %d outside [1, 64]", power_iters);
+  const size_t need = mcs::pddp_workspace_bytes(desc->batch, desc->heads, desc->seqlen, desc->head_dim, group_size);
+  if (ws_bytes < need) return fail(MCS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!ws || !aligned16(ws)) return fail(MCS_ERR_INVALID_ARGUMENT, "ws is NULL or not 16-byte aligned");
+  return hip_status(mcs::run_pddp((const uint16_t *)q, desc->stride_b, desc->stride_n, desc->stride_h,
+                                  desc->batch, desc->heads, desc->seqlen, desc->head_dim, group_size,
+                                  power_iters, perm, ws, ws_bytes, (hipStream_t)stream),
+                    "mcs_pddp_group");
+}
+
+mcs_status_t mcs_anchor_dense_lse(const mcs_attn_desc_t *desc, const void *q, const void *k,
+                                  const void *v, void *o, float *lse, mcs_stream_t stream) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_tensor(q, "q"));
+  MCS_TRY(check_tensor(k, "k"));
+  MCS_TRY(check_tensor(v, "v"));
+  MCS_TRY(check_tensor(o, "o"));
+  if (lse) MCS_TRY(check_ptr(lse, "lse"));
+  MCS_TRY(check_out_alias(desc, o, "o", {{q, "q"}, {k, "k"}, {v, "v"}}));
+  mcs::AttnArgs a = attn_args(desc);
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
+  a.out = (uint16_t *)o;
+  a.lse = lse;
+  a.rows = 128;
+  a.G = groups_of(desc, a.rows);
+  return hip_status(mcs::launch_attention(mcs::kModeDense, desc->head_dim, a, (hipStream_t)stream),
+                    "mcs_anchor_dense_lse");
+}
+
+mcs_status_t mcs_anchor_select_topk_workspace_size(const mcs_attn_desc_t *desc, int32_t group_size,
+                                                   int32_t topk, size_t *bytes) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_group(group_size));
+  MCS_TRY(check_topk(desc, topk));
+  if (!bytes) return fail(MCS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = (size_t)desc->batch * desc->heads * groups_of(desc, group_size) * desc->seqlen * sizeof(float);
+  return ok();
+}
+
+mcs_status_t mcs_anchor_select_topk(const mcs_attn_desc_t *desc, const void *q, const void *k,
+                                    const float *lse, const int32_t *perm, int32_t group_size,
+                                    int32_t topk, int32_t *kv_idx, float *group_mass, void *ws,
+                                    size_t ws_bytes, mcs_stream_t stream) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_group(group_size));
+  MCS_TRY(check_topk(desc, topk));
+  MCS_TRY(check_tensor(q, "q"));
+  MCS_TRY(check_tensor(k, "k"));
+  MCS_TRY(check_ptr(lse, "lse"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  MCS_TRY(check_ptr(kv_idx, "kv_idx"));
+  float *mass = group_mass;
+  if (mass) {
+    MCS_TRY(check_ptr(mass, "group_mass"));
+  } else {
+    const size_t need = (size_t)desc->batch * desc->heads * groups_of(desc, group_size) * desc->seqlen * sizeof(float);
+    if (ws_bytes < need) return fail(MCS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    MCS_TRY(check_ptr(ws, "ws"));
+    mass = (float *)ws;
+  }
+  mcs::SelectArgs a{};
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.lse = lse;
+  a.perm = perm;
+  a.mass = mass;
+  a.idx = kv_idx;
+  a.sb = desc->stride_b;
+  a.sn = desc->stride_n;
+  a.sh = desc->stride_h;
+  a.B = desc->batch;
+  a.H = desc->heads;
+  a.N = desc->seqlen;
+  a.T = group_size;
+  a.G = groups_of(desc, group_size);
+  a.K = topk;
+  a.scale_log2 = desc->scale * 1.4426950408889634f;
+  return hip_status(mcs::launch_select(desc->head_dim, a, (hipStream_t)stream), "mcs_anchor_select_topk");
+}
+
+mcs_status_t mcs_residual(const mcs_attn_desc_t *desc, const void *q, const void *k, const void *v,
+                          const void *o_dense, const int32_t *perm, int32_t group_size,
+                          const int32_t *kv_idx, int32_t topk, void *r, mcs_stream_t stream) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_group(group_size));
+  MCS_TRY(check_topk(desc, topk));
+  MCS_TRY(check_tensor(q, "q"));
+  MCS_TRY(check_tensor(k, "k"));
+  MCS_TRY(check_tensor(v, "v"));
+  MCS_TRY(check_tensor(o_dense, "o_dense"));
+  MCS_TRY(check_tensor(r, "r"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  MCS_TRY(check_ptr(kv_idx, "kv_idx"));
+  MCS_TRY(check_out_alias(desc, r, "r", {{q, "q"}, {k, "k"}, {v, "v"}, {o_dense, "o_dense"}}));
+  mcs::AttnArgs a = attn_args(desc);
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
+  a.aux = (const uint16_t *)o_dense;
+  a.out = (uint16_t *)r;
+  a.perm = perm;
+  a.idx = kv_idx;
+  a.rows = group_size;
+  a.G = groups_of(desc, group_size);
+  a.K = topk;
+  return hip_status(mcs::launch_attention(mcs::kModeResidual, desc->head_dim, a, (hipStream_t)stream),
+                    "mcs_residual");
+}
+
+mcs_status_t mcs_sparse_apply(const mcs_attn_desc_t *desc, const void *q, const void *k,
+                              const void *v, const int32_t *perm, int32_t group_size,
+                              const int32_t *kv_idx, int32_t topk, const void *r, void *o,
+                              mcs_stream_t stream) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_group(group_size));
+  MCS_TRY(check_topk(desc, topk));
+  MCS_TRY(check_tensor(q, "q"));
+  MCS_TRY(check_tensor(k, "k"));
+  MCS_TRY(check_tensor(v, "v"));
+  MCS_TRY(check_tensor(o, "o"));
+  if (r) MCS_TRY(check_tensor(r, "r"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  MCS_TRY(check_ptr(kv_idx, "kv_idx"));
+  MCS_TRY(check_out_alias(desc, o, "o", {{q, "q"}, {k, "k"}, {v, "v"}, {r, "r"}}));
+  mcs::AttnArgs a = attn_args(desc);
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
+  a.aux = (const uint16_t *)r;
+  a.out = (uint16_t *)o;
+  a.perm = perm;
+  a.idx = kv_idx;
+  a.rows = group_size;
+  a.G = groups_of(desc, group_size);
+  a.K = topk;
+  return hip_status(mcs::launch_attention(mcs::kModeSparse, desc->head_dim, a, (hipStream_t)stream),
+                    "mcs_sparse_apply");
+}
+
+}  // extern "C"

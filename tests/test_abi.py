@@ -1,0 +1,90 @@
+"""The C-ABI library loads, exports every symbol include/mcsparse.h declares,
+and rejects bad arguments before anything reaches the GPU (these calls make
+no HIP call, so they run on a host without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_diffusion_pddp_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "mcsparse.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mcs_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) == 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(s[0] for s in B.SIGNATURES) == names
+    assert lib.mcs_version() == 100
+
+
+def desc(B_=1, H=2, N=1000, d=128, scale=0.088):
+    return B.Desc(B_, H, N, d, N * H * d, H * d, d, scale)
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def status(lib, fn, *args):
+    return getattr(lib, fn)(*args)
+
+
+def test_validation_codes(lib):
+    d = desc()
+    null = None
+    s = lib.mcs_sparse_apply(None, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 10, None, FAKE, None)
+    assert s == 1 and b"desc" in lib.mcs_last_error()
+    bad = desc(d=96)
+    assert lib.mcs_sparse_apply(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 128, FAKE, 10, None, FAKE, None) == 2
+    assert lib.mcs_sparse_apply(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 96, FAKE, 10, None, FAKE, None) == 2
+    assert lib.mcs_sparse_apply(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 128, FAKE, 0, None, FAKE, None) == 1
+    assert lib.mcs_sparse_apply(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 128, FAKE, 1001, None, FAKE, None) == 1
+    assert b"topk" in lib.mcs_last_error()
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.mcs_sparse_apply(ctypes.byref(d), mis, FAKE, FAKE, FAKE, 128, FAKE, 10, None, FAKE, None) == 1
+    assert b"aligned" in lib.mcs_last_error()
+    # output aliasing an input
+    assert lib.mcs_sparse_apply(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 128, FAKE, 10, None, FAKE, None) == 1
+    assert b"overlaps" in lib.mcs_last_error()
+    assert lib.mcs_anchor_dense_lse(ctypes.byref(d), FAKE, FAKE, FAKE, null, None, None) == 1
+    bad_stride = B.Desc(1, 2, 1000, 128, 1000 * 2 * 128, 2 * 128 + 4, 128, 0.1)
+    assert lib.mcs_anchor_dense_lse(ctypes.byref(bad_stride), FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert lib.mcs_pddp_group(ctypes.byref(d), FAKE, 128, 0, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.mcs_pddp_group(ctypes.byref(d), FAKE, 128, 16, FAKE, FAKE, 16, None) == 3
+    assert lib.mcs_anchor_select_topk(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 128, 10, FAKE, None, FAKE, 16, None) == 3
+    assert lib.mcs_residual(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 0, FAKE, None) == 1
+
+
+def test_workspace_sizes(lib):
+    d = desc(H=12, N=32760)
+    n = ctypes.c_size_t()
+    assert lib.mcs_anchor_select_topk_workspace_size(ctypes.byref(d), 128, 4914, ctypes.byref(n)) == 0
+    assert n.value == 12 * 256 * 32760 * 4
+    assert lib.mcs_pddp_group_workspace_size(ctypes.byref(d), 128, ctypes.byref(n)) == 0
+    assert n.value > 12 * 32760 * 12  # projections + scratch order at least
+    small = desc(H=1, N=100)
+    assert lib.mcs_pddp_group_workspace_size(ctypes.byref(small), 128, ctypes.byref(n)) == 0
+    assert n.value > 0
+
+
+def test_rcache_argument_checks(lib):
+    h = ctypes.c_void_p()
+    assert lib.mcs_rcache_create(0, 1024, ctypes.byref(h)) == 1
+    assert lib.mcs_rcache_create(2, 1000, ctypes.byref(h)) == 1
+    assert lib.mcs_rcache_create(2, 1024, None) == 1
+    assert lib.mcs_rcache_store(None, 0, FAKE, None) == 1
+    assert lib.mcs_rcache_destroy(None) == 1
