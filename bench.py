@@ -1,0 +1,251 @@
+#!/usr/bin/env python
+"""Benchmark of the MC-Sparse hot path on one MI355X.
+
+One step = one anchor step (PDDP grouping, dense attention + LSE, exact
+top-K selection, residual) followed by the workload's reuse steps (sparse
+attention over the cached indices with freshly drifted Q/K/V, plus R), for
+one attention layer with all heads, on synthetic inputs already resident in
+HBM. Default workload: the Wan2.1-1.3B 480p shape (12 heads, N = 32760,
+d = 128, groups of 128, 15% density, 4 reuse steps).
+
+value: effective TFLOP/s of the reuse step, 4*B*H*N*K*d FLOPs per call
+(only selected keys, nominal rows) over the measured call time. The anchor
+step's milliseconds (per stage and total) are reported beside it.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "reuse-step sparse attn eff. TFLOP/s @15% density + anchor-step ms (1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_apply_wan480p_traffic.json")
+KERNEL_SOURCES = ["mcs_attention.hip", "mcs_common.hpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_attention_diffusion_pddp_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(per_launch_flops):
+    """HBM bytes per sparse_apply launch from committed rocprofv3 counters,
+    if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float, seed: int):
+    """The oracle, untuned, timed on the host on a bounded sample of the reuse
+    step: groups of head 0 (anchor metadata prepared by the oracle, untimed)."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle as O
+    from sparse_attention_diffusion_pddp_amd import synth
+
+    T, K, d = w.group_size, w.topk, w.head_dim
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = synth.make_qkv(w, seed=seed, heads=[0])
+    qt, kt, vt = synth.drift_qkv(w, (q, k, v), step=1, seed=seed, heads=[0])
+    hq, hk, hv, hqt, hkt, hvt = (t[0, :, 0].float().numpy().astype(np.float64) for t in (q, k, v, qt, kt, vt))
+    perm = O.pddp_group(hq, T)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    elapsed, flops, groups = 0.0, 0, 0
+    for g in range(w.groups):
+        rows = perm[g * T:(g + 1) * T]
+        od, L = O.dense_lse(hq[rows], hk, hv, scale)
+        idx = O.topk_select(O.group_mass(hq[rows], hk, L, scale), K)
+        R = O.residual(O.round_bf16(od), O.sparse_attention(hq[rows], hk, hv, idx, scale))
+        t0 = time.perf_counter()
+        O.reuse_output(hqt[rows], hkt, hvt, idx, R, scale)
+        elapsed += time.perf_counter() - t0
+        flops += 4 * len(rows) * K * d
+        groups += 1
+        if elapsed >= seconds:
+            break
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"reuse step of {w.name}: {groups} of {w.groups * w.heads} query groups (head 0), "
+                      f"{elapsed:.1f} s of oracle time, float64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="wan480p")
+    ap.add_argument("--density", type=int, default=None, help="override the density in percent")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (scales the rocprofv3 byte counters)")
+    args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        torch.cuda.set_device(0)
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": x.numel() * 4, "copies": 5}))
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the hot path shards by heads with no exchange, and this build measures one GPU's share.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_diffusion_pddp_amd import binding as mcs
+    from sparse_attention_diffusion_pddp_amd import metrics, synth
+
+    mcs.load()
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    if args.density is not None:
+        w = w.with_density(args.density)
+    B, H, N, d, T, K, G = w.batch, w.heads, w.seqlen, w.head_dim, w.group_size, w.topk, w.groups
+    R_STEPS = max(1, w.reuse_steps)
+
+    # ---- inputs, resident in HBM ------------------------------------------------
+    q, k, v = synth.make_qkv(w, seed=args.seed)
+    steps_in = [(q, k, v)]
+    for s in range(1, R_STEPS + 1):
+        steps_in.append(synth.drift_qkv(w, steps_in[-1], step=s, seed=args.seed))
+    dev = [tuple(t.cuda() for t in x) for x in steps_in]
+    del steps_in
+    dq, dk, dv = dev[0]
+    desc = mcs.desc_for(dq)
+    ws_pddp = torch.empty(mcs.pddp_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+    ws_sel = torch.empty(mcs.select_workspace_size(desc, T, K), dtype=torch.uint8, device="cuda")
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    o = torch.empty_like(dq)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, H, G, K), dtype=torch.int32, device="cuda")
+    r = torch.empty_like(dq)
+    ot = [torch.empty_like(dq) for _ in range(R_STEPS)]
+
+    stages = ["pddp", "dense_lse", "select_topk", "residual"] + [f"reuse{s}" for s in range(1, R_STEPS + 1)]
+
+    def step(ev):
+        ev[0].record()
+        mcs.pddp_group(dq, T, perm, ws_pddp)
+        ev[1].record()
+        mcs.anchor_dense_lse(dq, dk, dv, o, lse)
+        ev[2].record()
+        mcs.anchor_select_topk(dq, dk, lse, perm, T, K, idx, ws=ws_sel)
+        ev[3].record()
+        mcs.residual(dq, dk, dv, o, perm, T, idx, K, r)
+        ev[4].record()
+        for s in range(1, R_STEPS + 1):
+            qt, kt, vt = dev[s]
+            mcs.sparse_apply(qt, kt, vt, perm, T, idx, K, r, ot[s - 1])
+            ev[4 + s].record()
+
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+
+    for _ in range(args.warmup):
+        step(new_events())
+    torch.cuda.synchronize()
+
+    evs = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, name in enumerate(stages)}
+    anchor_ms = sum(stage_ms[s] for s in stages[:4])
+    reuse_ms = sum(stage_ms[f"reuse{s}"] for s in range(1, R_STEPS + 1)) / R_STEPS
+    flops = metrics.sparse_flops(B, H, N, K, d)
+    value = flops / (reuse_ms * 1e-3) / 1e12
+
+    # the same library's dense path (lse = NULL), the speedup denominator
+    o2 = torch.empty_like(dq)
+    de = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for _ in range(2):
+        mcs.anchor_dense_lse(dq, dk, dv, o2, None)
+    de[0].record()
+    for i in range(5):
+        mcs.anchor_dense_lse(dq, dk, dv, o2, None)
+        de[i + 1].record()
+    torch.cuda.synchronize()
+    dense_ms = de[0].elapsed_time(de[5]) / 5
+    density = K / N
+    rho, eta = metrics.kernel_speedup(dense_ms, reuse_ms, density)
+    anchor_only = stage_ms["select_topk"] + stage_ms["residual"] + stage_ms["pddp"]
+
+    traffic = load_traffic(flops)
+    achieved = value
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "attention_kernel<128,4,sparse> (mcs_sparse_apply)",
+                "per_launch_flop": flops, "avg_launch_ms": round(reuse_ms, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "seqlen": N, "grid": list(w.grid), "head_dim": d,
+                   "group_size": T, "density_pct": w.density_pct, "topk": K, "reuse_steps": R_STEPS,
+                   "seed": args.seed},
+        "anchor_step_ms": round(anchor_ms, 3),
+        "anchor_stages_ms": {s: round(stage_ms[s], 3) for s in stages[:4]},
+        "reuse_step_ms": round(reuse_ms, 4),
+        "dense_ms": round(dense_ms, 3),
+        "dense_tflops": round(metrics.dense_flops(B, H, N, d) / (dense_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense": round(rho, 3),
+        "eta": round(eta, 3),
+        "align": round(metrics.align_ratio(N, T, K, 64), 4),
+        "anchor_overhead_density_points": round(metrics.anchor_overhead_points(anchor_only, dense_ms), 3),
+        "pddp_ms_amortized_2_per_40": round(metrics.amortized_grouping_ms(stage_ms["pddp"]), 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
