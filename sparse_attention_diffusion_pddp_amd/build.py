@@ -24,9 +24,13 @@ SOURCES = ["mcs_api.cpp", "mcs_rcache.cpp", "mcs_attention.hip", "mcs_select.hip
 
 # packed fp32 instructions stay off (-packed-fp32-ops): the compiler would
 # otherwise form v_pk_{add,mul,fma}_f32 from plain float code.
+# Device code only: the kernels take finite data, so max/min need no NaN
+# canonicalisation (-fno-honor-nans, IEEE mode bit off); host code keeps
+# IEEE semantics (the API's argument checks use isfinite).
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xarch_device", "-fno-honor-nans", "-Xarch_device", "-mno-amdgpu-ieee",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

@@ -27,9 +27,9 @@ struct AttnCfg {
   static constexpr int NT = 64 * NW;          // threads
   static constexpr int KT = 64;               // keys per tile
   static constexpr int CH = D / 8;            // 16-byte chunks per row
-  static constexpr int KPT = KT * CH / NT;    // keys gathered per thread per tile
+  static constexpr int KPT = KT * CH / NT;    // keys gathered per thread per tile (K and V each)
   static constexpr int KROW = D + 8;          // LDS K row stride (bf16), +16 B pad
-  static constexpr int VROW = KT + 4;         // LDS V^T row stride (bf16), +8 B pad
+  static constexpr int VROW = KT + 8;         // LDS V^T row stride (bf16), +16 B pad
   static constexpr int KTILE = KT * KROW;
   static constexpr int VTILE = D * VROW;
   static constexpr int STAGE = KTILE + VTILE;
@@ -37,10 +37,25 @@ struct AttnCfg {
   static_assert(KPT == 2 || KPT == 4 || KPT == 8, "transpose width");
 };
 
+// The running max is only moved (and O, l rescaled) when a tile's max
+// exceeds it by more than this many powers of two; until then the
+// exponentials may reach 2^8, which fp32 and bf16 hold exactly as well as 1.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Column of key k (0..63) in the V^T tile: inside each 16-key block the
+// quads (4 keys) are stored in the order 0, 2, 1, 3, so that the 8 keys one
+// lane feeds to a 16-key MFMA step (keys 4h..4h+3 and 8+4h..8+4h+3) are
+// contiguous and one 16-byte LDS read fetches them.
+__device__ __forceinline__ int vt_col(int k) {
+  const int q = (k >> 2) & 3;
+  return (k & ~15) | ((((q & 1) << 1) | (q >> 1)) << 2) | (k & 3);
+}
+
 template <int D, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attention_kernel(AttnArgs a) {
   using C = AttnCfg<D, NW>;
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint32_t idx_s[2][C::KT];  // key rows of the next tiles
 
   const int nblocks = gridDim.x;
   const int work = xcd_remap(blockIdx.x, nblocks);
@@ -57,8 +72,11 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
 
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const bf16_t *qb = a.q + head_off;
-  const bf16_t *kb = a.k + head_off;
-  const bf16_t *vb = a.v + head_off;
+  // byte extent of this head's rows; buffer loads past it return zeros
+  const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const uint32_t extent = (uint32_t)(a.N - 1) * row_bytes + D * 2;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + head_off), 0, extent, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + head_off), 0, extent, kBufferFlags);
 
   // ---- this lane's query row -------------------------------------------
   const int row0 = g * a.rows;
@@ -81,30 +99,42 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
 
   // ---- key list ---------------------------------------------------------
   const int nkeys = (MODE == kModeDense) ? a.N : a.K;
-  const int32_t *kidx = (MODE == kModeDense) ? nullptr : a.idx + ((int64_t)bh * a.G + g) * a.K;
   const int ntiles = (nkeys + C::KT - 1) / C::KT;
+  const int32_t *idx_row = (MODE == kModeDense) ? a.idx : a.idx + ((int64_t)bh * a.G + g) * a.K;
+  // past the list the index buffer reads 0 (a valid row, masked later)
+  const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)idx_row, 0, (MODE == kModeDense) ? 0u : (uint32_t)a.K * 4u, kBufferFlags);
 
-  // loader: thread owns 16-byte chunk column c of keys kg*KPT .. kg*KPT+KPT-1
-  const int c = tid % C::CH;
-  const int kg = tid / C::CH;
+  // Loader mappings (KPT consecutive keys x one 16-byte chunk per thread):
+  //  K: chunk-minor, so 16 lanes fill one contiguous K row in LDS;
+  //  V: key-minor, so 16 lanes fill one contiguous V^T row in LDS
+  //     (conflict-free transposed writes).
+  const int kc = tid % C::CH, kk = (tid / C::CH) * C::KPT;
+  const int vq = tid % (C::KT / C::KPT), vc = tid / (C::KT / C::KPT);
+  const int vk = vq * C::KPT;
 
-  int ids[C::KPT], ids_next[C::KPT];
   u32x4 kreg[C::KPT], vreg[C::KPT];
+  uint32_t next_idx = 0;  // wave 0: key row of tile t+2 for this lane
 
-  auto load_ids = [&](int t, int *out) {
-#pragma unroll
-    for (int j = 0; j < C::KPT; ++j) {
-      int pos = t * C::KT + kg * C::KPT + j;
-      pos = pos < nkeys ? pos : nkeys - 1;  // tail: repeat a valid key, masked later
-      out[j] = (MODE == kModeDense) ? pos : kidx[pos];
+  auto key_row = [&](int t, int j) -> uint32_t {  // rows of tile t: LDS (sparse) or arithmetic (dense)
+    if (MODE == kModeDense) {
+      const int pos = t * C::KT + j;
+      return (uint32_t)(pos < a.N ? pos : a.N - 1);
     }
+    return idx_s[t & 1][j];
   };
-  auto issue = [&](const int *id) {
+  auto fetch_idx = [&](int t) {  // wave 0 lane l: index of key t*KT + l
+    if (MODE != kModeDense && wave == 0)
+      next_idx = __builtin_amdgcn_raw_buffer_load_b32(ri, (t * C::KT + lane) * 4, 0, 0);
+  };
+  auto store_idx = [&](int t) {
+    if (MODE != kModeDense && wave == 0) idx_s[t & 1][lane] = next_idx;
+  };
+  auto issue = [&](int t) {
 #pragma unroll
     for (int j = 0; j < C::KPT; ++j) {
-      const int64_t off = (int64_t)id[j] * a.sn + c * 8;
-      kreg[j] = *(const u32x4 *)(kb + off);
-      vreg[j] = *(const u32x4 *)(vb + off);
+      kreg[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, key_row(t, kk + j) * row_bytes + kc * 16, 0, 0);
+      vreg[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, key_row(t, vk + j) * row_bytes + vc * 16, 0, 0);
     }
   };
   auto commit = [&](int buf) {
@@ -112,10 +142,10 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
     bf16_t *vs = ks + C::KTILE;
 #pragma unroll
     for (int j = 0; j < C::KPT; ++j)
-      *(u32x4 *)(ks + (kg * C::KPT + j) * C::KROW + c * 8) = kreg[j];
-    // transpose: V^T[8c + e][kg*KPT + j]
+      *(u32x4 *)(ks + (kk + j) * C::KROW + kc * 8) = kreg[j];
+    // transpose into V^T[8*vc + e][vt_col(key)]
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {  // dim pair (8c+2m, 8c+2m+1)
+    for (int m = 0; m < 4; ++m) {  // dim pair (8vc+2m, 8vc+2m+1)
       uint32_t lo[C::KPT / 2], hi[C::KPT / 2];
 #pragma unroll
       for (int j = 0; j < C::KPT / 2; ++j) {
@@ -123,16 +153,18 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
         lo[j] = (x0 & 0xffffu) | (x1 << 16);
         hi[j] = (x0 >> 16) | (x1 & 0xffff0000u);
       }
-      bf16_t *d0 = vs + (8 * c + 2 * m) * C::VROW + kg * C::KPT;
+      bf16_t *d0 = vs + (8 * vc + 2 * m) * C::VROW;
       bf16_t *d1 = d0 + C::VROW;
       if (C::KPT == 2) {
-        *(uint32_t *)d0 = lo[0];
-        *(uint32_t *)d1 = hi[0];
+        const int col = vt_col(vk);
+        *(uint32_t *)(d0 + col) = lo[0];
+        *(uint32_t *)(d1 + col) = hi[0];
       } else {
 #pragma unroll
-        for (int j = 0; j < C::KPT / 2; j += 2) {
-          *(u32x2 *)(d0 + 2 * j) = u32x2{lo[j], lo[j + 1]};
-          *(u32x2 *)(d1 + 2 * j) = u32x2{hi[j], hi[j + 1]};
+        for (int j = 0; j < C::KPT / 2; j += 2) {  // one quad of keys per 8-byte write
+          const int col = vt_col(vk + 2 * j);
+          *(u32x2 *)(d0 + col) = u32x2{lo[j], lo[j + 1]};
+          *(u32x2 *)(d1 + col) = u32x2{hi[j], hi[j + 1]};
         }
       }
     }
@@ -141,25 +173,29 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-  float m_run = kNegBig;
+  float m_run = kNegBig;  // running max, log2 units
   float l_run = 0.f;
+  const float c2 = a.scale_log2;
+  const bool ragged = (nkeys % C::KT) != 0;
 
-  load_ids(0, ids);
-  issue(ids);
-  if (ntiles > 1) load_ids(1, ids_next);
+  // prologue: indices of tiles 0 and 1 into LDS, tile 0 into stage 0
+  fetch_idx(0);
+  store_idx(0);
+  fetch_idx(1);
+  store_idx(1);
+  __syncthreads();
+  issue(0);
   commit(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const bool more = (t + 1) < ntiles;
-    if (more) {
-      issue(ids_next);
-      if (t + 2 < ntiles) load_ids(t + 2, ids_next);
-    }
+    if (more) issue(t + 1);             // rows from idx_s[(t+1)&1]
+    if (t + 2 < ntiles) fetch_idx(t + 2);
     const bf16_t *ks = smem + (t & 1) * C::STAGE;
     const bf16_t *vs = ks + C::KTILE;
 
-    // S^T = K . Q^T for two 32-key blocks
+    // S^T = K . Q^T for two 32-key blocks (raw scores)
     f32x16 st[2];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -171,35 +207,37 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
         st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[kb2], 0, 0, 0);
       }
     }
-
-    // online softmax (base 2); this lane's values all belong to query l32
-    const int kbase = t * C::KT + 4 * hh;
-    float mt = kNegBig;
+    if (ragged && !more) {  // last tile: mask keys past the list
+      const int kbase = t * C::KT + 4 * hh;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = kbase + 32 * kb2 + 8 * (v >> 2) + (v & 3);
-        float x = st[kb2][v] * a.scale_log2;
-        x = key < nkeys ? x : kNegBig;
-        st[kb2][v] = x;
-        mt = fmaxf(mt, x);
-      }
+        for (int v = 0; v < 16; ++v)
+          if (kbase + 32 * kb2 + 8 * (v >> 2) + (v & 3) >= nkeys) st[kb2][v] = kNegBig;
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+
+    // online softmax, base 2; every value of this lane belongs to query l32
+    float mx = fmaxf(st[0][0], st[1][0]);
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(st[0][v], st[1][v]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_tile = mx * c2;
+    if (__any(m_tile > m_run + kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+    }
+    const float neg_m = -m_run;
 
     bf16x8 pf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(st[s >> 1][8 * (s & 1) + e] - m_new);
+        const float p = fast_exp2(__builtin_fmaf(st[s >> 1][8 * (s & 1) + e], c2, neg_m));
         l_run += p;
         pf[s][e] = (__bf16)p;
       }
@@ -208,18 +246,17 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
     // O^T += V^T . P^T
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const bf16_t *vrow = vs + (32 * db + l32) * C::VROW + 4 * hh;
+      const bf16_t *vrow = vs + (32 * db + l32) * C::VROW + 8 * hh;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x2 lo = *(const u32x2 *)(vrow + 16 * s);
-        const u32x2 hi = *(const u32x2 *)(vrow + 16 * s + 8);
-        const u32x4 vv = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[s],
-                                                           oacc[db], 0, 0, 0);
+        const bf16x8 vf = *(const bf16x8 *)(vrow + 16 * s);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[db], 0, 0, 0);
       }
     }
 
     if (more) commit((t + 1) & 1);
+    // idx_s[t&1] (tile t's rows) was last read by issue(t) one iteration ago
+    if (t + 2 < ntiles) store_idx(t + 2);
     __syncthreads();
   }
 

@@ -19,6 +19,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;  // masked score: exp2 of it is exactly 0
 
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format);
+// loads past num_records return zeros.
+constexpr int kBufferFlags = 0x00020000;
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
