@@ -16,6 +16,8 @@
 // MFMA operand layout used (32x32x16): lane l holds row/col (l % 32) and the
 // 8 reduction elements of half h = l / 32; accumulator value v of lane l is
 // row 8*(v/4) + 4*h + (v%4), col l % 32.
+#include <type_traits>
+
 #include "mcs_common.hpp"
 #include "mcs_internal.hpp"
 
@@ -75,8 +77,8 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
   // byte extent of this head's rows; buffer loads past it return zeros
   const uint32_t row_bytes = (uint32_t)a.sn * 2u;
   const uint32_t extent = (uint32_t)(a.N - 1) * row_bytes + D * 2;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + head_off), 0, extent, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + head_off), 0, extent, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(a.k + head_off, extent);
+  const __amdgpu_buffer_rsrc_t rv = uniform_rsrc(a.v + head_off, extent);
 
   // ---- this lane's query row -------------------------------------------
   const int row0 = g * a.rows;
@@ -102,8 +104,7 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
   const int ntiles = (nkeys + C::KT - 1) / C::KT;
   const int32_t *idx_row = (MODE == kModeDense) ? a.idx : a.idx + ((int64_t)bh * a.G + g) * a.K;
   // past the list the index buffer reads 0 (a valid row, masked later)
-  const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)idx_row, 0, (MODE == kModeDense) ? 0u : (uint32_t)a.K * 4u, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t ri = uniform_rsrc(idx_row, (MODE == kModeDense) ? 0u : (uint32_t)a.K * 4u);
 
   // Loader mappings (KPT consecutive keys x one 16-byte chunk per thread):
   //  K: chunk-minor, so 16 lanes fill one contiguous K row in LDS;
@@ -188,14 +189,15 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
   commit(0);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = (t + 1) < ntiles;
-    if (more) issue(t + 1);             // rows from idx_s[(t+1)&1]
+  // one 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T; the key
+  // mask exists only in the instantiation for the last tile
+  auto tile = [&](int t, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    if (!LAST) issue(t + 1);  // rows from idx_s[(t+1)&1]
     if (t + 2 < ntiles) fetch_idx(t + 2);
     const bf16_t *ks = smem + (t & 1) * C::STAGE;
     const bf16_t *vs = ks + C::KTILE;
 
-    // S^T = K . Q^T for two 32-key blocks (raw scores)
     f32x16 st[2];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
         st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[kb2], 0, 0, 0);
       }
     }
-    if (ragged && !more) {  // last tile: mask keys past the list
+    if (LAST && ragged) {
       const int kbase = t * C::KT + 4 * hh;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -243,7 +245,6 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
       }
     }
 
-    // O^T += V^T . P^T
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const bf16_t *vrow = vs + (32 * db + l32) * C::VROW + 8 * hh;
@@ -254,11 +255,13 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
       }
     }
 
-    if (more) commit((t + 1) & 1);
-    // idx_s[t&1] (tile t's rows) was last read by issue(t) one iteration ago
+    if (!LAST) commit((t + 1) & 1);
+    // idx_s[t&1] (tile t's rows) was last read by issue(t) one tile ago
     if (t + 2 < ntiles) store_idx(t + 2);
     __syncthreads();
-  }
+  };
+  for (int t = 0; t < ntiles - 1; ++t) tile(t, std::false_type{});
+  tile(ntiles - 1, std::true_type{});
 
   // ---- epilogue -----------------------------------------------------------
   l_run += __shfl_xor(l_run, 32);

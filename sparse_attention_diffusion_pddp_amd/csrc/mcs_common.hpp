@@ -23,6 +23,17 @@ constexpr float kNegBig = -1.0e30f;  // masked score: exp2 of it is exactly 0
 // loads past num_records return zeros.
 constexpr int kBufferFlags = 0x00020000;
 
+// A raw buffer resource whose base and size are wave-uniform (SGPRs). The
+// explicit readfirstlane keeps the compiler from treating the descriptor as
+// divergent, which would wrap every buffer load in a waterfall loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t v = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), 0, n, kBufferFlags);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
