@@ -34,6 +34,27 @@ def assert_close(got, want, name, denom=None, max_abs=MAX_ABS, rel_l2=REL_L2):
     return ma, rl
 
 
+def assert_close_residual(got, want_r, o_dense, name):
+    """R is a difference: near zero at high density, larger than O at very low
+    density. Its rel-L2 denominator is the larger of ||R|| and ||O_dense||."""
+    want_r = np.asarray(want_r, dtype=np.float64)
+    o_dense = np.asarray(o_dense, dtype=np.float64)
+    denom = want_r if np.linalg.norm(want_r) >= np.linalg.norm(o_dense) else o_dense
+    return assert_close(got, want_r, name, denom=denom)
+
+
+def assert_close_chained_reuse(got, want, r, name):
+    """Reuse output of a chained pipeline (each side fed its own R): R is
+    stored in bf16, so when |R| exceeds |O_t| (very low density) one bf16
+    step of R -- which the two sides may round differently, since their
+    O_dense differ by rounding -- lands in O_t. The rel-L2 denominator is the
+    larger of ||O_t|| and ||R||; max-abs stays absolute."""
+    want = np.asarray(want, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    denom = want if np.linalg.norm(want) >= np.linalg.norm(r) else r
+    return assert_close(got, want, name, denom=denom)
+
+
 def audit_topk(got, want, mass, K, N, name=""):
     """GPU index row vs the oracle's: valid (ascending, unique, in range, K of
     them) and equal as a set except for swaps across the cut whose oracle

@@ -156,7 +156,7 @@ def test_residual(c, lib):
     torch.cuda.synchronize()
     got = r.cpu().float().numpy()[0]
     for h in range(c.H):
-        U.assert_close(got[:, h], c.r[:, h], f"R h{h}", denom=c.o_dense[:, h])
+        U.assert_close_residual(got[:, h], c.r[:, h], c.o_dense[:, h], f"R h{h}")
 
 
 def test_sparse_apply_reuse(c, lib):
