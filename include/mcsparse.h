@@ -170,19 +170,20 @@ mcs_status_t mcs_sparse_apply(const mcs_attn_desc_t *desc, const void *q, const 
  * A cache holds `n_layers` blobs of `bytes_per_layer` bytes in pinned host
  * memory and owns two device slots used in turn (layer l uses slot l % 2),
  * plus the events that order them. It allocates (hipHostMalloc, hipMalloc)
- * in create and frees in destroy.
+ * in create and frees in destroy (which synchronises the device).
  *   store(l, src, s):     D2H copy of `bytes_per_layer` bytes from device
  *                         `src` into layer l's host blob, enqueued on s.
  *   prefetch(l, s):       H2D copy of layer l's blob into slot l % 2 on s
- *                         (a side stream); it first waits until the slot's
- *                         previous reader has finished (see acquire).
+ *                         (a side stream). If the slot was acquired since
+ *                         its last prefetch, the copy first waits for all
+ *                         work enqueued so far on the acquiring stream, so
+ *                         enqueue the slot's reader kernels before the next
+ *                         prefetch into that slot.
  *   acquire(l, s, &ptr):  makes stream s (the compute stream) wait for the
- *                         prefetch of layer l and returns the slot pointer;
- *                         it also marks, on s, the end of every earlier use
- *                         of the other slot. The pointer stays valid until
- *                         the prefetch of layer l + 2 is enqueued.
+ *                         prefetch of layer l and returns the slot pointer,
+ *                         valid until the next prefetch into the same slot.
  *   MCS_ERR_STATE: prefetch of a layer never stored, acquire of a layer
- *   whose prefetch was not enqueued last for that slot.
+ *   that is not the last prefetch into its slot.
  * ------------------------------------------------------------------------ */
 typedef struct mcs_rcache mcs_rcache_t;
 mcs_status_t mcs_rcache_create(int32_t n_layers, size_t bytes_per_layer, mcs_rcache_t **out);

@@ -57,6 +57,9 @@ mcs_status_t check_desc(const mcs_attn_desc_t *d) {
   if ((int64_t)d->batch * d->heads * d->seqlen > ((int64_t)1 << 31) - 1)
     return fail(MCS_ERR_INVALID_ARGUMENT, "batch*heads*seqlen exceeds 2^31-1");
   if (!std::isfinite(d->scale)) return fail(MCS_ERR_INVALID_ARGUMENT, "scale is not finite");
+  // the kernels address one head's rows with 32-bit byte offsets
+  if ((int64_t)(d->seqlen - 1) * d->stride_n * 2 + d->head_dim * 2 > (int64_t)UINT32_MAX)
+    return fail(MCS_ERR_UNSUPPORTED, "one head's rows span more than 4 GiB ((N-1)*stride_n too large)");
   return ok();
 }
 

@@ -23,8 +23,9 @@ struct mcs_rcache {
   char *host = nullptr;
   void *slot[2] = {nullptr, nullptr};
   hipEvent_t ready[2] = {nullptr, nullptr};  // prefetch into the slot finished
-  hipEvent_t freed[2] = {nullptr, nullptr};  // earlier readers of the slot finished
-  bool freed_recorded[2] = {false, false};
+  hipEvent_t freed[2] = {nullptr, nullptr};  // the slot's last reader finished
+  hipStream_t reader[2] = {nullptr, nullptr};
+  bool acquired[2] = {false, false};          // the slot has a reader since its last prefetch
   int32_t slot_layer[2] = {-1, -1};
   std::vector<char> stored;
 };
@@ -112,7 +113,13 @@ mcs_status_t mcs_rcache_prefetch(mcs_rcache_t *c, int32_t layer, mcs_stream_t st
   if (st != MCS_OK) return st;
   if (!c->stored[layer]) return fail(MCS_ERR_STATE, "layer %d was never stored", layer);
   const int s = layer & 1;
-  if (c->freed_recorded[s]) HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, c->freed[s], 0), "mcs_rcache_prefetch");
+  if (c->acquired[s]) {
+    // everything enqueued so far on the stream that last acquired this slot
+    // (its reader kernels) must finish before the slot is overwritten
+    HIP_TRY(hipEventRecord(c->freed[s], c->reader[s]), "mcs_rcache_prefetch");
+    HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, c->freed[s], 0), "mcs_rcache_prefetch");
+    c->acquired[s] = false;
+  }
   HIP_TRY(hipMemcpyAsync(c->slot[s], c->host + (size_t)layer * c->bytes, c->bytes, hipMemcpyHostToDevice,
                          (hipStream_t)stream),
           "mcs_rcache_prefetch");
@@ -128,10 +135,8 @@ mcs_status_t mcs_rcache_acquire(mcs_rcache_t *c, int32_t layer, mcs_stream_t str
   const int s = layer & 1;
   if (c->slot_layer[s] != layer) return fail(MCS_ERR_STATE, "layer %d is not the last prefetch into its slot", layer);
   HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, c->ready[s], 0), "mcs_rcache_acquire");
-  // everything enqueued on the compute stream so far (the readers of the
-  // other slot) must finish before that slot is refilled
-  HIP_TRY(hipEventRecord(c->freed[s ^ 1], (hipStream_t)stream), "mcs_rcache_acquire");
-  c->freed_recorded[s ^ 1] = true;
+  c->reader[s] = (hipStream_t)stream;
+  c->acquired[s] = true;
   *dev_ptr = c->slot[s];
   return MCS_OK;
 }
