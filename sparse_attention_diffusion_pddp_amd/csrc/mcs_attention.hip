@@ -25,18 +25,14 @@ namespace mcs {
 
 template <int D, int NW>
 struct AttnCfg {
-  static constexpr int TQ = 32 * NW;          // query rows per workgroup
-  static constexpr int NT = 64 * NW;          // threads
-  static constexpr int KT = 64;               // keys per tile
-  static constexpr int CH = D / 8;            // 16-byte chunks per row
-  static constexpr int KPT = KT * CH / NT;    // keys gathered per thread per tile (K and V each)
-  static constexpr int KROW = D + 8;          // LDS K row stride (bf16), +16 B pad
-  static constexpr int VROW = KT + 8;         // LDS V^T row stride (bf16), +16 B pad
-  static constexpr int KTILE = KT * KROW;
-  static constexpr int VTILE = D * VROW;
-  static constexpr int STAGE = KTILE + VTILE;
-  static_assert(NT % CH == 0 && (NT / CH) * KPT == KT, "loader mapping");
-  static_assert(KPT == 2 || KPT == 4 || KPT == 8, "transpose width");
+  static constexpr int TQ = 32 * NW;           // query rows per workgroup
+  static constexpr int NT = 64 * NW;           // threads
+  static constexpr int KT = 64;                // keys per tile
+  static constexpr int CH = D / 8;             // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;           // bytes per K or V row
+  static constexpr int TILEB = KT * ROWB;      // bytes of one K (or V) tile
+  static constexpr int LPW = TILEB / 1024 / NW;  // 1 KB LDS-DMA loads per wave per tensor
+  static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "loader mapping");
 };
 
 // The running max is only moved (and O, l rescaled) when a tile's max
@@ -44,20 +40,46 @@ struct AttnCfg {
 // exponentials may reach 2^8, which fp32 and bf16 hold exactly as well as 1.
 constexpr float kRescaleLog2 = 8.0f;
 
-// Column of key k (0..63) in the V^T tile: inside each 16-key block the
-// quads (4 keys) are stored in the order 0, 2, 1, 3, so that the 8 keys one
-// lane feeds to a 16-key MFMA step (keys 4h..4h+3 and 8+4h..8+4h+3) are
-// contiguous and one 16-byte LDS read fetches them.
-__device__ __forceinline__ int vt_col(int k) {
-  const int q = (k >> 2) & 3;
-  return (k & ~15) | ((((q & 1) << 1) | (q >> 1)) << 2) | (k & 3);
+// K and V tiles sit in LDS row-major (one row = one key), each 16-byte chunk
+// c of row k stored at chunk c ^ swz(k). With it, the 32 keys x one chunk of
+// a K fragment read and the 4 keys x 32 bytes of a transposing V read both
+// spread over all banks.
+template <int CH>
+__device__ __forceinline__ int swz(int k) {
+  return (((k & 3) << 1) | ((k >> 2) & 1) | (((k >> 3) & 1) << 3)) & (CH - 1);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Inside each group of 16
+// lanes, with M[j] the four 16-bit values at lane j's address, lane i
+// receives M[4e + i/4][i % 4] as element e (e = 0..3).
+// (The host compilation pass of this file never sees gfx950 builtins: a
+// kernel template mentioning them would silently lose its host launch stub.)
+__device__ __forceinline__ s16x4 lds_read_tr16(const bf16_t *p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+#else
+  return s16x4{};
+#endif
+}
+
+// 16-byte buffer load of each lane straight into LDS at lds + 16 * lane.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+#endif
 }
 
 template <int D, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, 2) void attention_kernel(AttnArgs a) {
   using C = AttnCfg<D, NW>;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * C::STAGE];
-  __shared__ __attribute__((aligned(16))) uint32_t idx_s[2][C::KT];  // key rows of the next tiles
+  // two pipeline stages as separate LDS objects, so the compiler can tell
+  // the stage being filled by DMA from the one being read
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[2 * C::TILEB / 2];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[2 * C::TILEB / 2];
+  __shared__ __attribute__((aligned(16))) uint32_t idx_s[2][C::KT];  // key rows of upcoming tiles
 
   const int nblocks = gridDim.x;
   const int work = xcd_remap(blockIdx.x, nblocks);
@@ -68,7 +90,7 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -106,18 +128,8 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
   // past the list the index buffer reads 0 (a valid row, masked later)
   const __amdgpu_buffer_rsrc_t ri = uniform_rsrc(idx_row, (MODE == kModeDense) ? 0u : (uint32_t)a.K * 4u);
 
-  // Loader mappings (KPT consecutive keys x one 16-byte chunk per thread):
-  //  K: chunk-minor, so 16 lanes fill one contiguous K row in LDS;
-  //  V: key-minor, so 16 lanes fill one contiguous V^T row in LDS
-  //     (conflict-free transposed writes).
-  const int kc = tid % C::CH, kk = (tid / C::CH) * C::KPT;
-  const int vq = tid % (C::KT / C::KPT), vc = tid / (C::KT / C::KPT);
-  const int vk = vq * C::KPT;
-
-  u32x4 kreg[C::KPT], vreg[C::KPT];
   uint32_t next_idx = 0;  // wave 0: key row of tile t+2 for this lane
-
-  auto key_row = [&](int t, int j) -> uint32_t {  // rows of tile t: LDS (sparse) or arithmetic (dense)
+  auto key_row = [&](int t, int j) -> uint32_t {
     if (MODE == kModeDense) {
       const int pos = t * C::KT + j;
       return (uint32_t)(pos < a.N ? pos : a.N - 1);
@@ -131,43 +143,19 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
   auto store_idx = [&](int t) {
     if (MODE != kModeDense && wave == 0) idx_s[t & 1][lane] = next_idx;
   };
-  auto issue = [&](int t) {
+  // DMA tile t's K and V rows into a stage: wave w fills LDS slots
+  // [(w*LPW + i)*64, +64) of 16 bytes; slot S is row S/CH, stored chunk S%CH,
+  // which holds logical chunk (S%CH) ^ swz(row)
+  auto issue = [&](int t, bf16_t *stage) {
 #pragma unroll
-    for (int j = 0; j < C::KPT; ++j) {
-      kreg[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, key_row(t, kk + j) * row_bytes + kc * 16, 0, 0);
-      vreg[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, key_row(t, vk + j) * row_bytes + vc * 16, 0, 0);
-    }
-  };
-  auto commit = [&](int buf) {
-    bf16_t *ks = smem + buf * C::STAGE;
-    bf16_t *vs = ks + C::KTILE;
-#pragma unroll
-    for (int j = 0; j < C::KPT; ++j)
-      *(u32x4 *)(ks + (kk + j) * C::KROW + kc * 8) = kreg[j];
-    // transpose into V^T[8*vc + e][vt_col(key)]
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {  // dim pair (8vc+2m, 8vc+2m+1)
-      uint32_t lo[C::KPT / 2], hi[C::KPT / 2];
-#pragma unroll
-      for (int j = 0; j < C::KPT / 2; ++j) {
-        const uint32_t x0 = vreg[2 * j][m], x1 = vreg[2 * j + 1][m];
-        lo[j] = (x0 & 0xffffu) | (x1 << 16);
-        hi[j] = (x0 >> 16) | (x1 & 0xffff0000u);
-      }
-      bf16_t *d0 = vs + (8 * vc + 2 * m) * C::VROW;
-      bf16_t *d1 = d0 + C::VROW;
-      if (C::KPT == 2) {
-        const int col = vt_col(vk);
-        *(uint32_t *)(d0 + col) = lo[0];
-        *(uint32_t *)(d1 + col) = hi[0];
-      } else {
-#pragma unroll
-        for (int j = 0; j < C::KPT / 2; j += 2) {  // one quad of keys per 8-byte write
-          const int col = vt_col(vk + 2 * j);
-          *(u32x2 *)(d0 + col) = u32x2{lo[j], lo[j + 1]};
-          *(u32x2 *)(d1 + col) = u32x2{hi[j], hi[j + 1]};
-        }
-      }
+    for (int i = 0; i < C::LPW; ++i) {
+      const int slot = (wave * C::LPW + i) * 64 + lane;
+      const int row = slot / C::CH;
+      const int chunk = (slot % C::CH) ^ swz<C::CH>(row);
+      const uint32_t off = key_row(t, row) * row_bytes + chunk * 16;
+      char *kdst = (char *)stage + (wave * C::LPW + i) * 1024;
+      buffer_load_lds16(rk, kdst, off);
+      buffer_load_lds16(rv, kdst + C::TILEB, off);
     }
   };
 
@@ -179,33 +167,24 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
   const float c2 = a.scale_log2;
   const bool ragged = (nkeys % C::KT) != 0;
 
-  // prologue: indices of tiles 0 and 1 into LDS, tile 0 into stage 0
-  fetch_idx(0);
-  store_idx(0);
-  fetch_idx(1);
-  store_idx(1);
-  __syncthreads();
-  issue(0);
-  commit(0);
-  __syncthreads();
-
-  // one 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T; the key
-  // mask exists only in the instantiation for the last tile
-  auto tile = [&](int t, auto last_tag) {
+  // one 64-key tile on `cur` while `nxt` fills with tile t+1:
+  // S^T = K Q^T, online softmax, O^T += V^T P^T
+  auto tile = [&](int t, const bf16_t *cur, bf16_t *nxt, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
-    if (!LAST) issue(t + 1);  // rows from idx_s[(t+1)&1]
+    if (!LAST) issue(t + 1, nxt);  // rows from idx_s[(t+1)&1]
     if (t + 2 < ntiles) fetch_idx(t + 2);
-    const bf16_t *ks = smem + (t & 1) * C::STAGE;
-    const bf16_t *vs = ks + C::KTILE;
+    const bf16_t *ks = cur;
+    const bf16_t *vs = cur + C::TILEB / 2;
 
     f32x16 st[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      st[kb2] = f32x16{};
-      const bf16_t *krow = ks + (32 * kb2 + l32) * C::KROW + 8 * hh;
+    for (int kb2 = 0; kb2 < 2; ++kb2) st[kb2] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 kf = *(const bf16x8 *)(krow + 16 * s);
+    for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int r = 32 * kb2 + l32;
+        const bf16x8 kf = *(const bf16x8 *)(ks + r * D + (((2 * s + hh) ^ swz<C::CH>(r)) << 3));
         st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[kb2], 0, 0, 0);
       }
     }
@@ -245,23 +224,57 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
       }
     }
 
+    // O^T += V^T . P^T. The V^T operand of lane (dim 32db + l32, half hh)
+    // for 16-key step s holds keys 16s + 4hh + {0..3} and 16s + 8 + 4hh +
+    // {0..3} (the order of P's slots): two transposing reads, each over
+    // 4 keys x 16 dims per 16-lane group.
+    const int grp = lane >> 4, j = lane & 15;
+    const int dim = 16 * (grp & 1) + 4 * (j & 3);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const bf16_t *vrow = vs + (32 * db + l32) * C::VROW + 8 * hh;
+    for (int s = 0; s < 4; ++s) {
+      const int key0 = 16 * s + 4 * hh + (j >> 2);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 vf = *(const bf16x8 *)(vrow + 16 * s);
+      for (int db = 0; db < D / 32; ++db) {
+        const int dd = 32 * db + dim;
+        const int k1 = key0 + 8;
+        const s16x4 lo = lds_read_tr16(vs + key0 * D + ((((dd >> 3) ^ swz<C::CH>(key0)) << 3) | (dd & 7)));
+        const s16x4 hi = lds_read_tr16(vs + k1 * D + ((((dd >> 3) ^ swz<C::CH>(k1)) << 3) | (dd & 7)));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                                         lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[db], 0, 0, 0);
       }
     }
 
-    if (!LAST) commit((t + 1) & 1);
-    // idx_s[t&1] (tile t's rows) was last read by issue(t) one tile ago
-    if (t + 2 < ntiles) store_idx(t + 2);
-    __syncthreads();
+    if (!LAST) {
+      // idx_s[t&1] (tile t's rows) was last read by issue(t) one tile ago
+      if (t + 2 < ntiles) store_idx(t + 2);
+      // this wave's DMA into `nxt` has landed (vmcnt(0)); then every wave's
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    }
   };
-  for (int t = 0; t < ntiles - 1; ++t) tile(t, std::false_type{});
-  tile(ntiles - 1, std::true_type{});
+
+  // prologue: rows of tiles 0 and 1, tile 0 into stage 0
+  fetch_idx(0);
+  store_idx(0);
+  fetch_idx(1);
+  store_idx(1);
+  __syncthreads();
+  issue(0, st0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  // stages alternate st0 / st1; unrolled by two so each tile's stage is static
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    tile(t, st0, st1, std::false_type{});
+    tile(t + 1, st1, st0, std::false_type{});
+  }
+  if (ntiles - t == 2) {
+    tile(t, st0, st1, std::false_type{});
+    tile(t + 1, st1, st0, std::true_type{});
+  } else {
+    tile(t, st0, st1, std::true_type{});
+  }
 
   // ---- epilogue -----------------------------------------------------------
   l_run += __shfl_xor(l_run, 32);
@@ -269,6 +282,17 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
   const float inv = 1.0f / l_run;
   const int64_t row_off = head_off + (int64_t)token * a.sn;
   bf16_t *orow = a.out + row_off;
+  // all of this lane's R / O_dense values are loaded before any store: out
+  // and aux may not be assumed disjoint by the compiler, which would
+  // otherwise serialise each load behind the previous store
+  u32x2 aux[D / 32][4];
+  const bool has_aux = (MODE == kModeResidual) || (MODE == kModeSparse && a.aux != nullptr);
+  if (has_aux) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) aux[db][qd] = *(const u32x2 *)(a.aux + row_off + 32 * db + 8 * qd + 4 * hh);
+  }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -276,20 +300,15 @@ __global__ __launch_bounds__(64 * NW, (D == 128 && NW == 2) ? 1 : 2) void attent
       const int d0 = 32 * db + 8 * qd + 4 * hh;
       float o0 = oacc[db][4 * qd + 0] * inv, o1 = oacc[db][4 * qd + 1] * inv;
       float o2 = oacc[db][4 * qd + 2] * inv, o3 = oacc[db][4 * qd + 3] * inv;
-      if (MODE == kModeSparse) {
-        if (a.aux) {
-          const u32x2 r = *(const u32x2 *)(a.aux + row_off + d0);
-          o0 += bf16_to_f32(r[0] & 0xffffu);
-          o1 += bf16_to_f32(r[0] >> 16);
-          o2 += bf16_to_f32(r[1] & 0xffffu);
-          o3 += bf16_to_f32(r[1] >> 16);
+      if (has_aux) {
+        const u32x2 r = aux[db][qd];
+        const float a0 = bf16_to_f32(r[0] & 0xffffu), a1 = bf16_to_f32(r[0] >> 16);
+        const float a2 = bf16_to_f32(r[1] & 0xffffu), a3 = bf16_to_f32(r[1] >> 16);
+        if (MODE == kModeSparse) {  // O + R
+          o0 += a0; o1 += a1; o2 += a2; o3 += a3;
+        } else {                    // R = O_dense - O
+          o0 = a0 - o0; o1 = a1 - o1; o2 = a2 - o2; o3 = a3 - o3;
         }
-      } else if (MODE == kModeResidual) {
-        const u32x2 od = *(const u32x2 *)(a.aux + row_off + d0);
-        o0 = bf16_to_f32(od[0] & 0xffffu) - o0;
-        o1 = bf16_to_f32(od[0] >> 16) - o1;
-        o2 = bf16_to_f32(od[1] & 0xffffu) - o2;
-        o3 = bf16_to_f32(od[1] >> 16) - o3;
       }
       *(u32x2 *)(orow + d0) = u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
     }

@@ -23,6 +23,12 @@ constexpr float kNegBig = -1.0e30f;  // masked score: exp2 of it is exactly 0
 // loads past num_records return zeros.
 constexpr int kBufferFlags = 0x00020000;
 
+// s_waitcnt immediate for vmcnt(0) with expcnt / lgkmcnt left at their
+// maximum (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]). Used after LDS-DMA loads, whose completion the compiler
+// does not track through registers.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // A raw buffer resource whose base and size are wave-uniform (SGPRs). The
 // explicit readfirstlane keeps the compiler from treating the descriptor as
 // divergent, which would wrap every buffer load in a waterfall loop.
