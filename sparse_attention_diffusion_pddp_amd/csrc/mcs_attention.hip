@@ -5,12 +5,13 @@
 // One workgroup owns one tile of query rows: a PDDP query group (sparse,
 // residual) or a run of consecutive tokens (dense). Each of its waves owns 32
 // query rows. The key loop walks 64-key tiles; a tile's K rows and V rows are
-// gathered by index (or read contiguously, dense) with 16-byte loads, staged
-// in LDS (K row-major, V transposed so keys are contiguous) with one tile of
-// prefetch in registers, and consumed by v_mfma_f32_32x32x16_bf16:
+// gathered by index (or read contiguously, dense) with LDS-DMA buffer loads
+// straight into one of two LDS stages (the next tile fills one stage while
+// the current one is consumed), and consumed by v_mfma_f32_32x32x16_bf16:
 //   S^T (keys x queries) = K . Q^T        -- D/16 MFMAs per 32-key block
 //   O^T (dims x queries) += V^T . P^T     -- P^T comes straight from S^T's
-//                                            accumulator layout, no shuffle.
+//                                            accumulator layout, no shuffle;
+//                                            V^T through transposing LDS reads.
 // Online softmax in base 2 (scale * log2 e folded in), fp32 statistics.
 //
 // MFMA operand layout used (32x32x16): lane l holds row/col (l % 32) and the
@@ -176,74 +177,79 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_kernel(AttnArgs a) {
     const bf16_t *ks = cur;
     const bf16_t *vs = cur + C::TILEB / 2;
 
+    // halves A (keys 0..31) and B (32..63): QK(B) is issued next to A's
+    // exponentials and PV(A) next to B's max, so MFMA and VALU work of one
+    // wave interleave
     f32x16 st[2];
+    const int grp = lane >> 4, j = lane & 15;
+    const int dim = 16 * (grp & 1) + 4 * (j & 3);
+    auto qkh = [&](int kb2) {
+      st[kb2] = f32x16{};
+      const int r = 32 * kb2 + l32;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) st[kb2] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const int r = 32 * kb2 + l32;
+      for (int s = 0; s < D / 16; ++s) {
         const bf16x8 kf = *(const bf16x8 *)(ks + r * D + (((2 * s + hh) ^ swz<C::CH>(r)) << 3));
         st[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[kb2], 0, 0, 0);
       }
-    }
-    if (LAST && ragged) {
-      const int kbase = t * C::KT + 4 * hh;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      if (LAST && ragged) {
+        const int kbase = t * C::KT + 4 * hh + 32 * kb2;
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (kbase + 32 * kb2 + 8 * (v >> 2) + (v & 3) >= nkeys) st[kb2][v] = kNegBig;
-    }
-
-    // online softmax, base 2; every value of this lane belongs to query l32
-    float mx = fmaxf(st[0][0], st[1][0]);
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(st[0][v], st[1][v]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_tile = mx * c2;
-    if (__any(m_tile > m_run + kRescaleLog2)) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-    }
-    const float neg_m = -m_run;
-
-    bf16x8 pf[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(__builtin_fmaf(st[s >> 1][8 * (s & 1) + e], c2, neg_m));
-        l_run += p;
-        pf[s][e] = (__bf16)p;
+          if (kbase + 8 * (v >> 2) + (v & 3) >= nkeys) st[kb2][v] = kNegBig;
       }
-    }
-
-    // O^T += V^T . P^T. The V^T operand of lane (dim 32db + l32, half hh)
-    // for 16-key step s holds keys 16s + 4hh + {0..3} and 16s + 8 + 4hh +
-    // {0..3} (the order of P's slots): two transposing reads, each over
-    // 4 keys x 16 dims per 16-lane group.
-    const int grp = lane >> 4, j = lane & 15;
-    const int dim = 16 * (grp & 1) + 4 * (j & 3);
+    };
+    auto rescale = [&](int kb2) {
+      float mx = st[kb2][0];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int key0 = 16 * s + 4 * hh + (j >> 2);
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, st[kb2][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_tile = mx * c2;
+      if (__any(m_tile > m_run + kRescaleLog2)) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int dd = 32 * db + dim;
+        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+      }
+    };
+    auto exps = [&](int kb2, bf16x8 *pf) {
+      const float neg_m = -m_run;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(st[kb2][8 * s2 + e], c2, neg_m));
+          l_run += p;
+          pf[s2][e] = (__bf16)p;
+        }
+    };
+    auto pvh = [&](int kb2, const bf16x8 *pf) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int s = 2 * kb2 + s2;
+        const int key0 = 16 * s + 4 * hh + (j >> 2);
         const int k1 = key0 + 8;
-        const s16x4 lo = lds_read_tr16(vs + key0 * D + ((((dd >> 3) ^ swz<C::CH>(key0)) << 3) | (dd & 7)));
-        const s16x4 hi = lds_read_tr16(vs + k1 * D + ((((dd >> 3) ^ swz<C::CH>(k1)) << 3) | (dd & 7)));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
-                                                         lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s], oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int dd = 32 * db + dim;
+          const s16x4 lo = lds_read_tr16(vs + key0 * D + ((((dd >> 3) ^ swz<C::CH>(key0)) << 3) | (dd & 7)));
+          const s16x4 hi = lds_read_tr16(vs + k1 * D + ((((dd >> 3) ^ swz<C::CH>(k1)) << 3) | (dd & 7)));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                                           lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s2], oacc[db], 0, 0, 0);
+        }
       }
-    }
+    };
+    bf16x8 pfa[2], pfb[2];
+    qkh(0);
+    rescale(0);
+    qkh(1);
+    exps(0, pfa);
+    pvh(0, pfa);
+    rescale(1);
+    exps(1, pfb);
+    pvh(1, pfb);
 
     if (!LAST) {
       // idx_s[t&1] (tile t's rows) was last read by issue(t) one tile ago
