@@ -56,6 +56,49 @@ def load_traffic(per_launch_flops):
     return t.get("bytes_per_launch")
 
 
+def write_traffic(fetch_dir, write_dir, fetch_copy_dir, write_copy_dir, kernel="attention_kernel<128, 4, 1>"):
+    """Turns four rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE of this bench
+    with --steps 1 --warmup 0, and of --copy-calibration) into the traffic
+    file read above: KiB per dispatch of `kernel`, each counter scaled by
+    what it reads for a plain 1 GiB device copy. Needs no GPU."""
+    import collections
+    import csv
+    import glob
+
+    def per_dispatch(d, counter, match):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals = collections.defaultdict(list)
+        for f in files:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] == counter and match in r["Kernel_Name"]:
+                        vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        if len(vals) != 1:
+            raise SystemExit(f"{counter} in {d}: expected one kernel matching {match!r}, found {sorted(vals)}")
+        v = next(iter(vals.values()))
+        return sum(v) / len(v), len(v)
+
+    copy_kib = (1 << 30) / 1024
+    fetch, n_f = per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
+    write, n_w = per_dispatch(write_dir, "WRITE_SIZE", kernel)
+    fetch_c, _ = per_dispatch(fetch_copy_dir, "FETCH_SIZE", "copyBuffer")
+    write_c, _ = per_dispatch(write_copy_dir, "WRITE_SIZE", "copyBuffer")
+    fs, ws = copy_kib / fetch_c, copy_kib / write_c
+    out = {"kernel": f"{kernel} (mcs_sparse_apply), wan480p 15%", "kernel_hash": kernel_hash(),
+           "dispatches": {"fetch": n_f, "write": n_w},
+           "fetch_kib_per_launch": round(fetch, 1), "write_kib_per_launch": round(write, 1),
+           "copy_calibration_kib": {"bytes_copied_kib": copy_kib, "fetch_kib": round(fetch_c, 1),
+                                    "write_kib": round(write_c, 1)},
+           "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+           "bytes_per_launch": int(round((fetch * fs + write * ws) * 1024))}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def cpu_baseline(w, seconds: float, seed: int):
     """The oracle, untuned, timed on the host on a bounded sample of the reuse
     step: groups of head 0 (anchor metadata prepared by the oracle, untimed)."""
@@ -207,7 +250,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales the rocprofv3 byte counters)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "FETCH_COPY", "WRITE_COPY"),
+                    help="summarise four rocprofv3 --pmc output folders into the committed traffic file")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        return write_traffic(*args.write_traffic)
 
     if args.copy_calibration:
         import torch
