@@ -238,6 +238,80 @@ def run_schedule(args):
     print(json.dumps(out), flush=True)
 
 
+def run_kernel_only(args, w):
+    """Wan14B-720p-shaped layer: the sparse_apply kernel alone on groups and
+    indices prepared by the library's own anchor calls (untimed), next to the
+    same library's dense attention (paper landing page, Table 6: kernel
+    speedup with selection and grouping excluded). Timed with and without
+    the +R epilogue; rho / eta use the plain sparse kernel."""
+    import torch
+
+    from sparse_attention_diffusion_pddp_amd import binding as mcs
+    from sparse_attention_diffusion_pddp_amd import metrics, synth
+
+    mcs.load()
+    torch.cuda.set_device(0)
+    B, H, N, d, T, K, G = w.batch, w.heads, w.seqlen, w.head_dim, w.group_size, w.topk, w.groups
+    q, k, v = (t.cuda() for t in synth.make_qkv(w, seed=args.seed))
+    desc = mcs.desc_for(q)
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    idx = torch.empty((B, H, G, K), dtype=torch.int32, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    r = torch.empty_like(q)
+    out = torch.empty_like(q)
+    ws = torch.empty(mcs.pddp_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+    mcs.pddp_group(q, T, perm, ws)
+    del ws
+    mcs.anchor_dense_lse(q, k, v, o, lse)
+    ws = torch.empty(mcs.select_workspace_size(desc, T, K), dtype=torch.uint8, device="cuda")
+    mcs.anchor_select_topk(q, k, lse, perm, T, K, idx, ws=ws)
+    del ws
+    mcs.residual(q, k, v, o, perm, T, idx, K, r)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    def timed(fn, n, warm):
+        for _ in range(warm):
+            fn()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        e[0].record()
+        for i in range(n):
+            fn()
+            e[i + 1].record()
+        torch.cuda.synchronize()
+        return sum(e[i].elapsed_time(e[i + 1]) for i in range(n)) / n
+
+    t0 = time.perf_counter()
+    sparse_r_ms = timed(lambda: mcs.sparse_apply(q, k, v, perm, T, idx, K, r, out), args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+    sparse_ms = timed(lambda: mcs.sparse_apply(q, k, v, perm, T, idx, K, None, out), args.steps, args.warmup)
+    dense_ms = timed(lambda: mcs.anchor_dense_lse(q, k, v, o, None), 3, 1)
+    flops = metrics.sparse_flops(B, H, N, K, d)
+    value = flops / (sparse_r_ms * 1e-3) / 1e12
+    rho, eta = metrics.kernel_speedup(dense_ms, sparse_ms, K / N)
+    out_line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "seqlen": N, "grid": list(w.grid), "head_dim": d,
+                   "group_size": T, "density_pct": w.density_pct, "topk": K, "kernel_only": True, "seed": args.seed},
+        "sparse_apply_ms": round(sparse_r_ms, 4),
+        "sparse_kernel_ms": round(sparse_ms, 4),
+        "sparse_kernel_tflops": round(flops / (sparse_ms * 1e-3) / 1e12, 2),
+        "dense_ms": round(dense_ms, 3),
+        "dense_tflops": round(metrics.dense_flops(B, H, N, d) / (dense_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense": round(rho, 3),
+        "eta": round(eta, 3),
+        "align": round(metrics.align_ratio(N, T, K, 64), 4),
+        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attention_kernel<128,4,sparse> (mcs_sparse_apply)", "per_launch_flop": flops,
+                     "avg_launch_ms": round(sparse_r_ms, 4)},
+    }
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +351,12 @@ def main():
 
     if args.workload == "voxel3d":
         return run_schedule(args)
+    if args.workload == "wan720p":
+        from sparse_attention_diffusion_pddp_amd import synth
+        w = synth.WORKLOADS["wan720p"]
+        if args.density is not None:
+            w = w.with_density(args.density)
+        return run_kernel_only(args, w)
 
     import torch
 

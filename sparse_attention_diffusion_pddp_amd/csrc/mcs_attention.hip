@@ -164,7 +164,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   float m_run = kNegBig;  // running max, log2 units
-  float l_run = 0.f;
+  // running row sum, compensated (Kahan): over tens of thousands of keys
+  // the mass of the many small probabilities would otherwise fall below
+  // half an ulp of the sum and be lost, biasing the LSE low. l_cmp holds
+  // minus the part of the added values that l_run could not take up.
+  float l_run = 0.f, l_cmp = 0.f;
   const float c2 = a.scale_log2;
   const bool ragged = (nkeys % C::KT) != 0;
 
@@ -209,20 +213,26 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_kernel(AttnArgs a) {
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
+        l_cmp *= alpha;
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
       }
     };
     auto exps = [&](int kb2, bf16x8 *pf) {
       const float neg_m = -m_run;
+      float lt = 0.f;  // this half tile's 16 values
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = fast_exp2(__builtin_fmaf(st[kb2][8 * s2 + e], c2, neg_m));
-          l_run += p;
+          lt += p;
           pf[s2][e] = (__bf16)p;
         }
+      const float y = lt - l_cmp;
+      const float sum = l_run + y;
+      l_cmp = (sum - l_run) - y;
+      l_run = sum;
     };
     auto pvh = [&](int kb2, const bf16x8 *pf) {
 #pragma unroll
@@ -283,6 +293,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_kernel(AttnArgs a) {
   }
 
   // ---- epilogue -----------------------------------------------------------
+  l_run -= l_cmp;
   l_run += __shfl_xor(l_run, 32);
   if (!row_valid) return;
   const float inv = 1.0f / l_run;

@@ -1,9 +1,14 @@
-"""GPU parity at the benchmark's full size and launch configuration.
+"""GPU parity at the workloads' full sizes and launch configuration.
 
-Wan2.1-1.3B-480p-shaped layer: 12 heads, N = 32760 (21x30x52 grid),
-d = 128, groups of 128 (the last holds 120 rows), K = 4914 (15%), plus one
-drifted reuse step. The whole pipeline runs on the GPU exactly as bench.py
-launches it. The oracle then checks:
+Three layer shapes, each with all heads, d = 128, groups of 128:
+  * wan480p: 12 heads, N = 32760 (21x30x52 grid, last group 120 rows),
+    K = 4914 (15%), plus one drifted reuse step;
+  * wan720p: 40 heads, N = 75600 (21x45x80, last group 80 rows),
+    K = 15120 (20%), reuse on the anchor's own inputs (no drift);
+  * longvideo: 24 heads, N = 98304 (24x64x64), K = 14746 (15%), plus one
+    drifted reuse step.
+The whole pipeline runs on the GPU exactly as bench.py launches it. The
+oracle then checks:
   * PDDP groups of two full heads, exactly;
   * dense O / LSE, indices, R and the reuse output on sampled groups (the
     first, a middle and the short last group of each sampled head), each GPU
@@ -26,17 +31,27 @@ from tests import parity_util as U
 
 pytestmark = pytest.mark.gpu
 
-HEADS = (0, 7)
-GROUPS = (0, 101, 255)
+# workload: (sampled heads, sampled groups; -1 = the last, possibly short, group)
+SAMPLES = {
+    "wan480p": ((0, 7), (0, 101, -1)),
+    "wan720p": ((0, 29), (0, 300, -1)),
+    "longvideo": ((0, 17), (0, 500, -1)),
+}
 
 
-@pytest.fixture(scope="module")
-def run(lib):
-    w = synth.WORKLOADS["wan480p"]
+@pytest.fixture(scope="module", params=list(SAMPLES))
+def run(request, lib):
+    name = request.param
+    w = synth.WORKLOADS[name]
     B, H, N, d, T, K, G = w.batch, w.heads, w.seqlen, w.head_dim, w.group_size, w.topk, w.groups
-    print(f"\n[wan480p full size: H={H} N={N} d={d} T={T} K={K}]", flush=True)
+    HEADS = SAMPLES[name][0]
+    GROUPS = tuple(g % G for g in SAMPLES[name][1])
+    print(f"\n[{name} full size: H={H} N={N} d={d} T={T} K={K}]", flush=True)
     q, k, v = synth.make_qkv(w, seed=3)
-    qt, kt, vt = synth.drift_qkv(w, (q, k, v), step=1, seed=3)
+    if w.drift > 0:
+        qt, kt, vt = synth.drift_qkv(w, (q, k, v), step=1, seed=3)
+    else:
+        qt, kt, vt = q, k, v
     dq, dk, dv, dqt, dkt, dvt = (x.cuda() for x in (q, k, v, qt, kt, vt))
     desc = mcs.desc_for(dq)
     ws = torch.empty(mcs.pddp_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
@@ -54,7 +69,7 @@ def run(lib):
     mcs.sparse_apply(dqt, dkt, dvt, perm, T, idx, K, r, ot)
     torch.cuda.synchronize()
     gpu = {"perm": perm.cpu().numpy()[0], "o": o.cpu(), "lse": lse.cpu().numpy()[0], "idx": idx.cpu().numpy()[0],
-           "mass_sum": mass.double().sum(dim=-1).cpu().numpy()[0]}
+           "mass_sum": mass.sum(dim=-1, dtype=torch.float64).cpu().numpy()[0]}
     del mass
     torch.cuda.empty_cache()
 
@@ -101,11 +116,13 @@ def run(lib):
     torch.cuda.synchronize()
     iso = {"idx": idx_iso.cpu().numpy()[0], "r": r_iso.cpu(), "ot": ot_iso.cpu(),
            "mass": {(h, g): mass_iso[0, h, g].double().cpu().numpy() for h in HEADS for g in GROUPS}}
-    return dict(w=w, gpu=gpu, orc=orc, iso=iso)
+    del mass_iso
+    torch.cuda.empty_cache()
+    return dict(w=w, gpu=gpu, orc=orc, iso=iso, heads=HEADS, groups=GROUPS)
 
 
 def test_groups_exact_full_heads(run):
-    for h in HEADS:
+    for h in run["heads"]:
         got = run["gpu"]["perm"][h]
         assert np.array_equal(got, run["orc"][h]), f"head {h}: first difference at {np.argmax(got != run['orc'][h])}"
 
@@ -127,8 +144,8 @@ def test_perm_and_index_properties_all_groups(run):
 
 def test_dense_sampled_rows(run):
     o = run["gpu"]["o"]
-    for h in HEADS:
-        for g in GROUPS:
+    for h in run["heads"]:
+        for g in run["groups"]:
             e = run["orc"][(h, g)]
             U.assert_close(o[0, e["rows"], h].float().numpy(), e["od"], f"O h{h} g{g}")
             U.assert_close(run["gpu"]["lse"][h, e["rows"]], e["L"], f"LSE h{h} g{g}", max_abs=U.LSE_ABS, rel_l2=1e-4)
@@ -137,8 +154,8 @@ def test_dense_sampled_rows(run):
 def test_select_sampled_groups(run):
     w = run["w"]
     swaps = 0
-    for h in HEADS:
-        for g in GROUPS:
+    for h in run["heads"]:
+        for g in run["groups"]:
             e = run["orc"][(h, g)]
             gm = run["iso"]["mass"][(h, g)]
             assert np.all(np.abs(gm - e["A"]) <= 1e-5 * e["A"] + 1e-7)
@@ -149,16 +166,16 @@ def test_select_sampled_groups(run):
 
 
 def test_residual_sampled_groups(run):
-    for h in HEADS:
-        for g in GROUPS:
+    for h in run["heads"]:
+        for g in run["groups"]:
             e = run["orc"][(h, g)]
             got = run["iso"]["r"][0, e["rows"], h].float().numpy()
             U.assert_close_residual(got, e["R"], e["od"], f"R h{h} g{g}")
 
 
 def test_reuse_sampled_groups(run):
-    for h in HEADS:
-        for g in GROUPS:
+    for h in run["heads"]:
+        for g in run["groups"]:
             e = run["orc"][(h, g)]
             got = run["iso"]["ot"][0, e["rows"], h].float().numpy()
             U.assert_close(got, e["out"], f"O_t h{h} g{g}")
