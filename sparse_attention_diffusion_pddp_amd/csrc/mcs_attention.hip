@@ -66,6 +66,21 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const bf16_t *p) {
 #endif
 }
 
+// Every lane gets {x of its lane in the low half (lanes 0-31), x of its lane
+// in the high half}: one v_permlane32_swap on two copies of x instead of an
+// LDS round trip. Written as inline asm because this toolchain's builtin for
+// the instruction returns the first register's result for both outputs.
+// The s_nops cover the VALU-write-then-permlane wait states.
+__device__ __forceinline__ void cross_half(float x, float &lo, float &hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  lo = x;
+  hi = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
+#else
+  lo = hi = x;
+#endif
+}
+
 // 16-byte buffer load of each lane straight into LDS at lds + 16 * lane.
 __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -206,8 +221,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_kernel(AttnArgs a) {
       float mx = st[kb2][0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) mx = fmaxf(mx, st[kb2][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_tile = mx * c2;
+      float mlo, mhi;
+      cross_half(mx, mlo, mhi);
+      const float m_tile = fmaxf(mlo, mhi) * c2;
       if (__any(m_tile > m_run + kRescaleLog2)) {
         const float m_new = fmaxf(m_run, m_tile);
         const float alpha = fast_exp2(m_run - m_new);
@@ -293,8 +309,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_kernel(AttnArgs a) {
   }
 
   // ---- epilogue -----------------------------------------------------------
-  l_run -= l_cmp;
-  l_run += __shfl_xor(l_run, 32);
+  {
+    float llo, lhi;
+    cross_half(l_run - l_cmp, llo, lhi);
+    l_run = llo + lhi;
+  }
   if (!row_valid) return;
   const float inv = 1.0f / l_run;
   const int64_t row_off = head_off + (int64_t)token * a.sn;
