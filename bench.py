@@ -32,7 +32,7 @@ METRIC = "reuse-step sparse attn eff. TFLOP/s @15% density + anchor-step ms (1 G
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_apply_wan480p_traffic.json")
-KERNEL_SOURCES = ["mcs_attention.hip", "mcs_common.hpp"]
+KERNEL_SOURCES = ["mcs_attention.hip", "mcs_common.hpp", "mcs_lds.hpp"]
 
 
 def kernel_hash() -> str:

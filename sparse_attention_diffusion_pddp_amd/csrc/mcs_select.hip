@@ -4,37 +4,45 @@
 // (ties -> lower key index), stored ascending.
 //
 // mass_kernel: one workgroup per (b, h, g). Each wave holds 32 of the group's
-// query rows as MFMA A-operands; 64-key tiles of K stream through LDS (one
-// tile prefetched in registers). S = Q . K^T via v_mfma_f32_32x32x16_bf16
-// leaves every lane with 16 query rows of ONE key, so the column sum over the
-// wave is 16 local adds plus one cross-half add; the 4 (or 2) waves' partial
-// sums meet in LDS and are added in a fixed order (no atomics).
+// query rows as MFMA A-operands; 64-key tiles of K arrive by LDS-DMA (16
+// bytes per lane straight into LDS, chunks XOR-swizzled per row) in two
+// stages, the next tile loading while the current one is used. S = Q . K^T
+// via v_mfma_f32_32x32x16_bf16 leaves every lane with 16 query rows of ONE
+// key, so the column sum over the wave is 16 local adds plus one
+// cross-half add; the 4 (or 2) waves' partial sums meet in LDS and are added
+// in a fixed order (no atomics).
 //
 // topk_kernel: one workgroup per (b, h, g). Radix select (4 passes of 8 bits,
 // most significant first) finds the K-th largest mass; a single ordered pass
 // with ballot prefix counts then keeps every key above it and the
 // lowest-index keys equal to it, writing their indices in ascending order.
+#include <type_traits>
+
 #include "mcs_common.hpp"
 #include "mcs_internal.hpp"
+#include "mcs_lds.hpp"
 
 namespace mcs {
 
 template <int D, int NW>
 struct MassCfg {
   static constexpr int NT = 64 * NW;
-  static constexpr int TQ = 32 * NW;
-  static constexpr int KT = 64;
-  static constexpr int CH = D / 8;
-  static constexpr int KPT = KT * CH / NT;
-  static constexpr int KROW = D + 8;
-  static constexpr int KTILE = KT * KROW;
-  static_assert((NT / CH) * KPT == KT, "loader mapping");
+  static constexpr int KT = 64;                  // keys per tile
+  static constexpr int CH = D / 8;               // 16-byte chunks per row
+  static constexpr int TILEB = KT * D * 2;       // bytes of one K tile
+  static constexpr int LPW = TILEB / 1024 / NW;  // 1 KB LDS-DMA loads per wave
+  static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "loader mapping");
 };
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void mass_kernel(SelectArgs a) {
+// four workgroups per CU (34.5 KB of LDS each at d = 128): at 128 VGPRs the
+// waves' exponentials and MFMAs overlap better than at two workgroups
+__global__ __launch_bounds__(64 * NW, 4) void mass_kernel(SelectArgs a) {
   using C = MassCfg<D, NW>;
-  __shared__ __attribute__((aligned(16))) bf16_t ksm[2 * C::KTILE];
+  // two stages as separate LDS objects, so the compiler can tell the stage
+  // being filled by DMA from the one being read
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[C::KT * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[C::KT * D];
   __shared__ float partial[2][NW][C::KT];
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
@@ -42,15 +50,18 @@ __global__ __launch_bounds__(64 * NW, 2) void mass_kernel(SelectArgs a) {
   const int g = work - bh * a.G;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const bf16_t *qb = a.q + head_off;
-  const bf16_t *kbase = a.k + head_off;
   const int32_t *pr = a.perm + (int64_t)bh * a.N;
   const float *lse = a.lse + (int64_t)bh * a.N;
   const int row0 = g * a.T;
+  const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const uint32_t extent = (uint32_t)(a.N - 1) * row_bytes + D * 2;
+  const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(a.k + head_off, extent);
 
   // A-operand rows: query wave*32 + l32 of the group
   bf16x8 qf[D / 16];
@@ -71,65 +82,75 @@ __global__ __launch_bounds__(64 * NW, 2) void mass_kernel(SelectArgs a) {
     const bool ok = r < a.T && pos < a.N;
     l2[v] = ok ? lse[pr[pos]] * kLog2e : 1.0e30f;  // invalid row: P = 0
   }
+  const float c2 = a.scale_log2;
 
   const int ntiles = (a.N + C::KT - 1) / C::KT;
-  const int c = tid % C::CH, kg = tid / C::CH;
-  u32x4 kreg[C::KPT];
-  auto issue = [&](int t) {
+  // DMA of tile t's K rows: slot S of the stage is row S / CH, stored chunk
+  // S % CH, holding logical chunk (S % CH) ^ swz(row); rows past N repeat
+  // the last key (their sums are not written)
+  auto issue = [&](int t, bf16_t *stage) {
 #pragma unroll
-    for (int j = 0; j < C::KPT; ++j) {
-      int key = t * C::KT + kg * C::KPT + j;
-      key = key < a.N ? key : a.N - 1;
-      kreg[j] = *(const u32x4 *)(kbase + (int64_t)key * a.sn + c * 8);
+    for (int i = 0; i < C::LPW; ++i) {
+      const int slot = (wave * C::LPW + i) * 64 + lane;
+      const int row = slot / C::CH;
+      const int chunk = (slot % C::CH) ^ swz<C::CH>(row);
+      const int key = t * C::KT + row;
+      const uint32_t off = (uint32_t)(key < a.N ? key : a.N - 1) * row_bytes + chunk * 16;
+      buffer_load_lds16(rk, (char *)stage + (wave * C::LPW + i) * 1024, off);
     }
-  };
-  auto commit = [&](int buf) {
-    bf16_t *ks = ksm + buf * C::KTILE;
-#pragma unroll
-    for (int j = 0; j < C::KPT; ++j) *(u32x4 *)(ks + (kg * C::KPT + j) * C::KROW + c * 8) = kreg[j];
   };
 
   float *mass_row = a.mass + ((int64_t)bh * a.G + g) * a.N;
-  issue(0);
-  commit(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) issue(t + 1);
-    // finish the previous tile's cross-wave sum
-    if (t > 0 && tid < C::KT) {
-      const int key = (t - 1) * C::KT + tid;
+  auto finish = [&](int t) {  // tile t's column sums over the waves, fixed order
+    if (tid < C::KT) {
+      const int key = t * C::KT + tid;
       float s = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) s += partial[(t - 1) & 1][w][tid];
+      for (int w = 0; w < NW; ++w) s += partial[t & 1][w][tid];
       if (key < a.N) mass_row[key] = s;
     }
-    const bf16_t *ks = ksm + (t & 1) * C::KTILE;
+  };
+  auto tile = [&](int t, const bf16_t *cur, bf16_t *nxt, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    if (!LAST) issue(t + 1, nxt);
+    if (t > 0) finish(t - 1);
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb = 0; kb < 2; ++kb) {
       f32x16 st = f32x16{};
-      const bf16_t *krow = ks + (32 * kb2 + l32) * C::KROW + 8 * hh;
+      const int r = 32 * kb + l32;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 kf = *(const bf16x8 *)(krow + 16 * s);
+        const bf16x8 kf = *(const bf16x8 *)(cur + r * D + (((2 * s + hh) ^ swz<C::CH>(r)) << 3));
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[s], kf, st, 0, 0, 0);
       }
       float cs = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) cs += fast_exp2(st[v] * a.scale_log2 - l2[v]);
-      cs += __shfl_xor(cs, 32);
-      if (hh == 0) partial[t & 1][wave][32 * kb2 + l32] = cs;
+      for (int v = 0; v < 16; ++v) cs += fast_exp2(__builtin_fmaf(st[v], c2, -l2[v]));
+      float lo, hi;
+      cross_half(cs, lo, hi);
+      if (hh == 0) partial[t & 1][wave][r] = lo + hi;
     }
-    if (more) commit((t + 1) & 1);
+    // this wave's DMA into `nxt` has landed; then every wave's, and every
+    // wave's partial sums are in LDS
+    if (!LAST) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+  };
+
+  issue(0, st0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    tile(t, st0, st1, std::false_type{});
+    tile(t + 1, st1, st0, std::false_type{});
   }
-  if (tid < C::KT) {
-    const int key = (ntiles - 1) * C::KT + tid;
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) s += partial[(ntiles - 1) & 1][w][tid];
-    if (key < a.N) mass_row[key] = s;
+  if (ntiles - t == 2) {
+    tile(t, st0, st1, std::false_type{});
+    tile(t + 1, st1, st0, std::true_type{});
+  } else {
+    tile(t, st0, st1, std::true_type{});
   }
+  finish(ntiles - 1);
 }
 
 // ---------------------------------------------------------------------------
