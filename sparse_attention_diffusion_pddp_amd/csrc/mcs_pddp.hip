@@ -26,6 +26,7 @@
 
 #include "mcs_common.hpp"
 #include "mcs_internal.hpp"
+#include "mcs_radix.hpp"
 
 namespace mcs {
 
@@ -277,25 +278,52 @@ __global__ __launch_bounds__(256) void cov_kernel(PddpArgs a) {
 }
 
 // ---- node direction: grid (nnodes, BH), 256 threads -------------------------
+// (value, index) max over a wave, lowest index among equal values
+__device__ __forceinline__ void wave_argmax(double &v, int &j) {
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) {
+    const double ov = __shfl_xor(v, s);
+    const int oj = __shfl_xor(j, s);
+    if (ov > v || (ov == v && oj < j)) {
+      v = ov;
+      j = oj;
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
+  constexpr int EPT = D * D / 256;  // covariance entries per thread
+  constexpr int PARTS = 256 / D;    // threads per column in the matrix-vector product
+  constexpr int JPP = D / PARTS;    // rows per part
   __shared__ double C[D * D];
-  __shared__ double u[D], w[D], red[256];
+  __shared__ double u[D], wpart[PARTS][D], red[4];
   __shared__ int jstar;
   const PLevel L = a.levels[a.level];
   const int bh = blockIdx.y;
   const int ln = blockIdx.x;
   const PNode nd = a.nodes[L.node0 + ln];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // covariance: add chunk partials in order (upper tiles), then mirror
-  const double *cp = a.cov_part + ((int64_t)bh * a.max_chunks + nd.chunk0) * D * D;
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, j = e - (e / D) * D;
-    if ((i >> 4) <= (j >> 4)) {
-      double s = 0.0;
-      for (int k = 0; k < nd.nchunks; ++k) s += cp[(int64_t)k * D * D + e];
-      C[e] = s / (double)nd.n;
+  // covariance: add the chunk partials (upper tiles) in chunk order, every
+  // entry of this thread accumulating at once so its loads overlap
+  {
+    const double *cp = a.cov_part + ((int64_t)bh * a.max_chunks + nd.chunk0) * D * D;
+    double acc[EPT];
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) acc[m] = 0.0;
+    for (int k = 0; k < nd.nchunks; ++k) {
+      const double *src = cp + (int64_t)k * D * D;
+#pragma unroll
+      for (int m = 0; m < EPT; ++m) {
+        const int e = tid + 256 * m;
+        if (((e / D) >> 4) <= ((e % D) >> 4)) acc[m] += src[e];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < EPT; ++m) {
+      const int e = tid + 256 * m;
+      if (((e / D) >> 4) <= ((e % D) >> 4)) C[e] = acc[m] / (double)nd.n;
     }
   }
   __syncthreads();
@@ -303,56 +331,86 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
     const int i = e / D, j = e - (e / D) * D;
     if ((i >> 4) > (j >> 4)) C[e] = C[j * D + i];
   }
-  // mean of the node for the projection kernel
+  // mean of the node for the projection kernel, partials in chunk order
   if (tid < D) {
     const double *mp = a.mean_part + ((int64_t)bh * a.max_chunks + nd.chunk0) * D + tid;
     double s = 0.0;
-    for (int k = 0; k < nd.nchunks; ++k) s += mp[(int64_t)k * D];
+    int k = 0;
+    for (; k + 8 <= nd.nchunks; k += 8) {
+      double v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = mp[(int64_t)(k + i) * D];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    for (; k < nd.nchunks; ++k) s += mp[(int64_t)k * D];
     a.mu[((int64_t)bh * a.max_nodes + ln) * D + tid] = s / (double)nd.n;
   }
   __syncthreads();
-  if (tid == 0) {
-    int best = 0;
-    double bv = C[0];
-    for (int j = 1; j < D; ++j) {
-      const double v = C[j * D + j];
-      if (v > bv) { bv = v; best = j; }
+  // start vector: e_j for the largest diagonal entry (lowest j on ties)
+  if (wave == 0) {
+    double v = C[lane * D + lane];
+    int j = lane;
+    if (D > 64) {
+      const double v2 = C[(lane + 64) * D + lane + 64];
+      if (v2 > v) {
+        v = v2;
+        j = lane + 64;
+      }
     }
-    jstar = best;
+    wave_argmax(v, j);
+    if (lane == 0) jstar = j;
   }
   __syncthreads();
   if (tid < D) u[tid] = (tid == jstar) ? 1.0 : 0.0;
   __syncthreads();
+  const int col = tid % D, part = tid / D;
   for (int it = 0; it < a.power_iters; ++it) {
-    double wi = 0.0;
-    if (tid < D) {
-      for (int j = 0; j < D; ++j) wi += C[j * D + tid] * u[j];  // C symmetric: column = row
-      w[tid] = wi;
+    // w = C u: thread (part, col) sums rows [part*JPP, +JPP) of column col
+    // (C is symmetric), two accumulators for ILP
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll 8
+    for (int jj = 0; jj < JPP; jj += 2) {
+      const int j = part * JPP + jj;
+      s0 += C[j * D + col] * u[j];
+      s1 += C[(j + 1) * D + col] * u[j + 1];
     }
-    red[tid] = (tid < D) ? wi * wi : 0.0;
+    wpart[part][col] = s0 + s1;
     __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-      if (tid < s) red[tid] += red[tid + s];
-      __syncthreads();
+    double w = 0.0, sq = 0.0;
+    if (tid < D) {
+#pragma unroll
+      for (int p = 0; p < PARTS; ++p) w += wpart[p][tid];
+      sq = w * w;
     }
-    const double nrm2 = red[0];
-    if (nrm2 == 0.0) {
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1) sq += __shfl_xor(sq, s);
+    if (lane == 0) red[wave] = sq;
+    __syncthreads();
+    double nrm2 = 0.0;
+#pragma unroll
+    for (int q = 0; q < (D + 63) / 64; ++q) nrm2 += red[q];
+    if (nrm2 == 0.0) {  // all queries equal: every projection will be 0
       if (tid < D) u[tid] = 0.0;
       break;
     }
-    const double nrm = sqrt(nrm2);
-    if (tid < D) u[tid] = w[tid] / nrm;
+    if (tid < D) u[tid] = w / sqrt(nrm2);
     __syncthreads();
   }
   __syncthreads();
-  if (tid == 0) {
-    int best = 0;
-    double bv = fabs(u[0]);
-    for (int j = 1; j < D; ++j) {
-      const double v = fabs(u[j]);
-      if (v > bv) { bv = v; best = j; }
+  // orientation: the largest-magnitude component positive (lowest j on ties)
+  if (wave == 0) {
+    double v = fabs(u[lane]);
+    int j = lane;
+    if (D > 64) {
+      const double v2 = fabs(u[lane + 64]);
+      if (v2 > v) {
+        v = v2;
+        j = lane + 64;
+      }
     }
-    jstar = best;
+    wave_argmax(v, j);
+    if (lane == 0) jstar = j;
   }
   __syncthreads();
   if (tid < D) {
@@ -433,16 +491,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(PddpArgs a) {
       if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t below = 0;
-      int d = 0;
-      for (; d < 255; ++d) {
-        if (below + hist[d] >= remaining) break;
-        below += hist[d];
-      }
-      sel_digit = (uint32_t)d;
-      sel_below = below;
-    }
+    if (wave == 0) radix_pick<false>(hist, remaining, &sel_digit, &sel_below);
     __syncthreads();
     prefix |= (uint64_t)sel_digit << shift;
     mask |= (uint64_t)255 << shift;

@@ -21,6 +21,7 @@
 #include "mcs_common.hpp"
 #include "mcs_internal.hpp"
 #include "mcs_lds.hpp"
+#include "mcs_radix.hpp"
 
 namespace mcs {
 
@@ -186,16 +187,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
       if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t above = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (above + hist[d] >= remaining) break;
-        above += hist[d];
-      }
-      sel_digit = (uint32_t)d;
-      sel_above = above;
-    }
+    if (wave == 0) radix_pick<true>(hist, remaining, &sel_digit, &sel_above);
     __syncthreads();
     prefix |= sel_digit << shift;
     mask |= 255u << shift;
