@@ -306,7 +306,10 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // covariance: add the chunk partials (upper tiles) in chunk order, every
-  // entry of this thread accumulating at once so its loads overlap
+  // entry of this thread accumulating at once so its loads overlap. The
+  // loads are unconditional (a partial's lower tiles are in the buffer but
+  // never written) and the lower-tile values are dropped by a select, so no
+  // branch serialises them.
   {
     const double *cp = a.cov_part + ((int64_t)bh * a.max_chunks + nd.chunk0) * D * D;
     double acc[EPT];
@@ -314,10 +317,13 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
     for (int m = 0; m < EPT; ++m) acc[m] = 0.0;
     for (int k = 0; k < nd.nchunks; ++k) {
       const double *src = cp + (int64_t)k * D * D;
+      double v[EPT];
+#pragma unroll
+      for (int m = 0; m < EPT; ++m) v[m] = src[tid + 256 * m];
 #pragma unroll
       for (int m = 0; m < EPT; ++m) {
         const int e = tid + 256 * m;
-        if (((e / D) >> 4) <= ((e % D) >> 4)) acc[m] += src[e];
+        acc[m] += (((e / D) >> 4) <= ((e % D) >> 4)) ? v[m] : 0.0;
       }
     }
 #pragma unroll
@@ -364,16 +370,19 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
   __syncthreads();
   if (tid < D) u[tid] = (tid == jstar) ? 1.0 : 0.0;
   __syncthreads();
+  // thread (part, col) keeps rows part, part + PARTS, ... of column col of
+  // C in registers for all iterations (C is symmetric: column = row)
   const int col = tid % D, part = tid / D;
+  double creg[JPP];
+#pragma unroll
+  for (int m = 0; m < JPP; ++m) creg[m] = C[(part + PARTS * m) * D + col];
   for (int it = 0; it < a.power_iters; ++it) {
-    // w = C u: thread (part, col) sums rows [part*JPP, +JPP) of column col
-    // (C is symmetric), two accumulators for ILP
+    // w = C u, this thread's rows; two accumulators for ILP
     double s0 = 0.0, s1 = 0.0;
-#pragma unroll 8
-    for (int jj = 0; jj < JPP; jj += 2) {
-      const int j = part * JPP + jj;
-      s0 += C[j * D + col] * u[j];
-      s1 += C[(j + 1) * D + col] * u[j + 1];
+#pragma unroll
+    for (int m = 0; m < JPP; m += 2) {
+      s0 += creg[m] * u[part + PARTS * m];
+      s1 += creg[m + 1] * u[part + PARTS * (m + 1)];
     }
     wpart[part][col] = s0 + s1;
     __syncthreads();
