@@ -134,32 +134,44 @@ def cpu_baseline(w, seconds: float, seed: int):
                       f"{elapsed:.1f} s of oracle time, float64 numpy"}
 
 
-def run_schedule(args):
-    """3D-latent layer stack (voxel3d): 12 steps x 40 layers, step 1 the
-    only anchor, layer 0 always dense, R offloaded to pinned host memory and
-    prefetched one layer ahead on a side stream (appendix Table 9; Table 8's
-    per-layer offload accounting). Activations: the anchor step's Q/K/V and
-    one drifted set reused by every later step (the cost of a call does not
-    depend on the values)."""
+def schedule_inputs(w, sched, seed):
+    """Activations for a layer-stack run: the first anchor's Q/K/V (also used
+    by the dense warm-up steps before it), then one drifted set between
+    anchors and one at each later anchor. The cost of a call does not depend
+    on the values; the drift keeps each anchor's metadata its own."""
+    from sparse_attention_diffusion_pddp_amd import synth
+
+    anchors = sorted(sched.anchor_steps)
+    sets = [synth.make_qkv(w, seed=seed)]
+    for i in range(1, 2 * len(anchors)):
+        sets.append(synth.drift_qkv(w, sets[-1], step=i, seed=seed))
+    dev = [tuple(t.cuda() for t in x) for x in sets]
+
+    def which(step):
+        if step <= anchors[0]:
+            return 0
+        n = sum(1 for a in anchors if a <= step)
+        return 2 * n - 2 if step in anchors else 2 * n - 1
+
+    return (lambda step, layer: dev[which(step)]), dev
+
+
+def run_schedule(args, w, sched, offload=True):
+    """A whole layer stack over all denoising steps through StackRunner
+    (appendix Table 9 schedules): dense warm-up steps and always-dense
+    layers, anchors that (re)build groups, indices and R, reuse layers in
+    between; R offloaded to pinned host memory and prefetched one layer
+    ahead on a side stream (Table 8's per-layer accounting)."""
     import torch
 
     from sparse_attention_diffusion_pddp_amd import binding as mcs
-    from sparse_attention_diffusion_pddp_amd import metrics, schedule, synth
+    from sparse_attention_diffusion_pddp_amd import metrics, schedule
 
     mcs.load()
     torch.cuda.set_device(0)
-    w = synth.WORKLOADS["voxel3d"]
-    if args.density is not None:
-        w = w.with_density(args.density)
     B, H, N, d, T, K = w.batch, w.heads, w.seqlen, w.head_dim, w.group_size, w.topk
-    sched = schedule.HY3D
-    anchor_in = synth.make_qkv(w, seed=args.seed)
-    reuse_in = synth.drift_qkv(w, anchor_in, step=1, seed=args.seed)
-    dev_a = tuple(t.cuda() for t in anchor_in)
-    dev_r = tuple(t.cuda() for t in reuse_in)
-    del anchor_in, reuse_in
-    runner = schedule.StackRunner(sched, dev_a[0].shape, T, K)
-    inputs = lambda step, layer: dev_a if step == 1 else dev_r
+    inputs, dev = schedule_inputs(w, sched, args.seed)
+    runner = schedule.StackRunner(sched, dev[0][0].shape, T, K, offload=offload)
     runner.run(inputs)  # warm-up pass of the whole schedule
     torch.cuda.synchronize()
     ev = {}
@@ -181,21 +193,30 @@ def run_schedule(args):
     runner.close()
 
     def avg(kind):
-        xs = [a.elapsed_time(b) for a, b in ev[kind]]
-        return sum(xs) / len(xs), len(xs)
+        xs = [a.elapsed_time(b) for a, b in ev.get(kind, [])]
+        return (sum(xs) / len(xs) if xs else 0.0), len(xs)
 
     reuse_ms, n_reuse = avg("reuse")
     pf_ms, n_pf = avg("prefetch")
     anchor_ms, n_anchor = avg("anchor")
+    pddp_ms, _ = avg("pddp")
     dense_ms, n_dense = avg("dense")
     step_ms = [a.elapsed_time(b) for a, b in ev["step"]]
+    plan = schedule.plan(sched)
+    kinds = {st: {a for s2, _, a in plan if s2 == st} for st in range(1, sched.steps + 1)}
+    anchor_steps = sorted(sched.anchor_steps)
+    reuse_steps = [st for st in range(1, sched.steps + 1) if kinds[st] == {schedule.DENSE, schedule.REUSE}]
+    warm_steps = [st for st in range(1, sched.steps + 1) if kinds[st] == {schedule.DENSE}]
+    step_avg = lambda sts: (sum(step_ms[st - 1] for st in sts) / len(sts)) if sts else 0.0
     flops = metrics.sparse_flops(B, H, N, K, d)
     value = flops / (reuse_ms * 1e-3) / 1e12
-    reuse_steps = step_ms[1:]
-    # a reuse step is one dense layer plus 39 reuse layers; what is left over
-    # is time the compute stream spent waiting for prefetches
+    # a reuse step is the dense layers plus the sparse layers' reuse calls;
+    # what is left over is time the compute stream spent waiting for prefetches
     n_sparse = len(runner.sparse_layers)
-    exposed = sum(s - dense_ms - n_sparse * reuse_ms for s in reuse_steps) / len(reuse_steps)
+    n_dl = len(sched.dense_layers)
+    exposed = (sum(step_ms[st - 1] - n_dl * dense_ms - n_sparse * reuse_ms for st in reuse_steps) / len(reuse_steps)
+               if reuse_steps else 0.0)
+    all_dense_ms = sched.steps * sched.layers * dense_ms
     r_bytes = runner.r_bytes
     out = {
         "metric": METRIC,
@@ -212,15 +233,22 @@ def run_schedule(args):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seqlen": N, "grid": list(w.grid), "head_dim": d,
                    "group_size": T, "density_pct": w.density_pct, "topk": K, "layers": sched.layers,
-                   "denoise_steps": sched.steps, "anchor_steps": list(sched.anchor_steps),
-                   "dense_layers": list(sched.dense_layers), "seed": args.seed},
+                   "denoise_steps": sched.steps, "warmup_steps": sched.warmup_steps,
+                   "anchor_steps": anchor_steps, "dense_layers": list(sched.dense_layers),
+                   "offload": offload, "seed": args.seed},
         "schedule_counts": {"dense": n_dense, "anchor": n_anchor, "reuse": n_reuse, "prefetch": n_pf,
-                            "store": len(ev["store"])},
-        "anchor_step_ms": round(step_ms[0], 3),
+                            "store": len(ev.get("store", []))},
+        "anchor_step_ms": [round(step_ms[st - 1], 3) for st in anchor_steps],
         "anchor_layer_ms": round(anchor_ms, 3),
-        "reuse_step_ms_avg": round(sum(reuse_steps) / len(reuse_steps), 3),
+        "pddp_layer_ms": round(pddp_ms, 3),
+        "pddp_ms_amortized_per_step": round(pddp_ms * len(anchor_steps) / max(1, sched.steps - sched.warmup_steps), 4),
+        "warmup_step_ms_avg": round(step_avg(warm_steps), 3),
+        "reuse_step_ms_avg": round(step_avg(reuse_steps), 3),
         "reuse_layer_ms": round(reuse_ms, 4),
         "dense_layer_ms": round(dense_ms, 3),
+        "denoise_ms": round(sum(step_ms), 1),
+        "all_dense_denoise_ms": round(all_dense_ms, 1),
+        "attention_speedup_vs_all_dense": round(all_dense_ms / sum(step_ms), 3),
         "table8_row": {"V_MB": round(r_bytes / 1e6, 1), "V_MiB": round(r_bytes / 2**20, 1),
                        "C_TFLOP": round(flops / 1e12, 3),
                        "C_over_V": round(metrics.offload_ratio(flops / 1e12, r_bytes / 2**20)),
@@ -229,7 +257,7 @@ def run_schedule(args):
                        "compute_ms": round(reuse_ms, 3),
                        "exposed_wait_ms_per_reuse_step": round(exposed, 3),
                        "hidden_per_layer": bool(h2d_ms <= reuse_ms),
-                       "hidden": bool(exposed <= 0.01 * sum(reuse_steps) / len(reuse_steps))},
+                       "hidden": bool(exposed <= 0.01 * step_avg(reuse_steps))},
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": "attention_kernel<128,4,sparse> (mcs_sparse_apply)", "per_launch_flop": flops,
@@ -322,6 +350,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--offload", choices=["auto", "on", "off"], default="auto",
+                    help="layer-stack workloads: R in pinned host memory with one-layer-ahead prefetch "
+                         "(auto: on for voxel3d, whose offload the schedule is taken from; off for wanvideo, "
+                         "whose 30 layers of R fit in HBM many times over)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales the rocprofv3 byte counters)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "FETCH_COPY", "WRITE_COPY"),
@@ -349,8 +381,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    if args.workload == "voxel3d":
-        return run_schedule(args)
+    if args.workload in ("voxel3d", "wanvideo"):
+        from sparse_attention_diffusion_pddp_amd import schedule, synth
+        name, sched = (("voxel3d", schedule.HY3D) if args.workload == "voxel3d"
+                       else ("wan480p", schedule.WAN_1_3B_VIDEO))
+        w = synth.WORKLOADS[name]
+        if args.density is not None:
+            w = w.with_density(args.density)
+        offload = args.offload == "on" or (args.offload == "auto" and args.workload == "voxel3d")
+        return run_schedule(args, w, sched, offload=offload)
     if args.workload == "wan720p":
         from sparse_attention_diffusion_pddp_amd import synth
         w = synth.WORKLOADS["wan720p"]

@@ -118,8 +118,9 @@ class StackRunner:
 
     def run(self, inputs, events=None, outputs=None):
         """Executes the plan. ``events`` (optional dict) collects per-call
-        (kind, start, end) CUDA events on the stream that ran the call, and
-        per-step ("step", start, end) on the compute stream; ``outputs``
+        (kind, start, end) CUDA events on the stream that ran the call (an
+        anchor call also gives its grouping as "pddp"), and per-step
+        ("step", start, end) on the compute stream; ``outputs``
         (optional dict) receives a copy of every layer output by (step, layer)."""
         compute = torch.cuda.current_stream()
         rec = events is not None
@@ -145,6 +146,7 @@ class StackRunner:
                 elif act == ANCHOR:
                     e0 = _ev(rec)
                     mcs.pddp_group(q, self.T, self.perm[layer], self.ws_pddp, self.power_iters)
+                    _push(events, "pddp", e0, _ev(rec))
                     mcs.anchor_dense_lse(q, k, v, self.o, self.lse)
                     mcs.anchor_select_topk(q, k, self.lse, self.perm[layer], self.T, self.K, self.idx[layer],
                                            ws=self.ws_sel)

@@ -60,3 +60,54 @@ def test_offloaded_stack_matches_device_resident(lib):
         R = O.residual(od[rows], O.sparse_attention(qa[rows], ka, va, sel, scale))
         want[rows] = O.reuse_output(qt[rows], kt, vt, sel, R, scale)
     U.assert_close(got, want, "stack reuse output")
+
+
+def test_refreshed_anchor_reuses_the_new_metadata(lib):
+    """Two anchors (Table 9's refresh): the reuse layers after the second
+    anchor use the groups, indices and R computed from that anchor's inputs,
+    those before it the first anchor's; warm-up steps and layer 0 stay dense.
+    Offloaded and device-resident R agree bitwise."""
+    sched = S.Schedule(steps=5, layers=3, dense_layers=(0,), warmup_steps=1, anchor_steps=(2, 4))
+    w = synth.small_workload(640, heads=2, head_dim=128, group_size=128, density_pct=20)
+    per_step = {1: synth.make_qkv(w, seed=33)}
+    for st in range(2, sched.steps + 1):
+        per_step[st] = synth.drift_qkv(w, per_step[st - 1], step=st - 1, seed=33)
+    dev = {st: tuple(t.cuda() for t in x) for st, x in per_step.items()}
+    inputs = lambda step, layer: dev[step]
+    shape = per_step[1][0].shape
+    c = S.counts(S.plan(sched))
+    assert c == {"dense": 3 + 4, "anchor": 4, "reuse": 4}
+    outs = {}
+    for offload in (True, False):
+        r = S.StackRunner(sched, shape, w.group_size, w.topk, offload=offload)
+        ev, out = {}, {}
+        r.run(inputs, events=ev, outputs=out)
+        torch.cuda.synchronize()
+        assert len(ev["anchor"]) == c["anchor"] and len(ev["reuse"]) == c["reuse"] and len(ev["dense"]) == c["dense"]
+        outs[offload] = out
+        r.close()
+    for key in outs[True]:
+        assert torch.equal(outs[True][key], outs[False][key]), key
+    scale = 1.0 / math.sqrt(w.head_dim)
+    h = 1
+    for anchor_step, reuse_step in ((2, 3), (4, 5)):
+        qa, ka, va = (U.head_np(t, 0, h) for t in per_step[anchor_step])
+        qt, kt, vt = (U.head_np(t, 0, h) for t in per_step[reuse_step])
+        perm = O.pddp_group(qa, w.group_size)
+        od, L = O.dense_lse(qa, ka, va, scale)
+        od = O.round_bf16(od)
+        want = np.zeros_like(od)
+        for g in range(w.groups):
+            rows = perm[g * w.group_size:(g + 1) * w.group_size]
+            sel = O.topk_select(O.group_mass(qa[rows], ka, L[rows], scale), w.topk)
+            R = O.residual(od[rows], O.sparse_attention(qa[rows], ka, va, sel, scale))
+            want[rows] = O.reuse_output(qt[rows], kt, vt, sel, R, scale)
+        got = outs[True][(reuse_step, 2)][0, :, h].float().cpu().numpy()
+        U.assert_close(got, want, f"reuse at step {reuse_step} after the anchor at step {anchor_step}")
+        # the anchor layer's output is the dense output
+        got_a = outs[True][(anchor_step, 2)][0, :, h].float().cpu().numpy()
+        U.assert_close(got_a, od, f"anchor output at step {anchor_step}")
+    # a warm-up step is dense
+    q1, k1, v1 = (U.head_np(t, 0, h) for t in per_step[1])
+    od1, _ = O.dense_lse(q1, k1, v1, scale)
+    U.assert_close(outs[True][(1, 1)][0, :, h].float().cpu().numpy(), O.round_bf16(od1), "warm-up dense")
