@@ -340,6 +340,82 @@ def run_kernel_only(args, w):
     print(json.dumps(out_line), flush=True)
 
 
+def run_variants(args, w):
+    """Selection variants on synthetic data, the ablation axes of the paper
+    landing page (Tables 3-4): query order (PDDP groups vs consecutive
+    tokens) x selection granularity (single keys vs 64-key blocks), at the
+    same realised density. Per variant: recall = mean over groups of the
+    selected keys' share of the group's exact probability mass; the sparse
+    output's relative L1 error against dense at the anchor (no R); and the
+    reuse output's error (sparse + R) against dense on the drifted steps.
+    Diagnostics only: the block variant picks its blocks with torch from the
+    library's exact group masses; the partial last block (N mod 64 keys) is
+    never a candidate, so every block variant keeps exactly K' keys."""
+    import torch
+
+    from sparse_attention_diffusion_pddp_amd import binding as mcs
+    from sparse_attention_diffusion_pddp_amd import synth
+
+    mcs.load()
+    torch.cuda.set_device(0)
+    B, H, N, d, T, K, G = w.batch, w.heads, w.seqlen, w.head_dim, w.group_size, w.topk, w.groups
+    BLK = 64
+    nb = max(1, round(K / BLK))
+    Kb = nb * BLK
+    steps = [synth.make_qkv(w, seed=args.seed)]
+    for s_ in range(1, max(1, w.reuse_steps) + 1):
+        steps.append(synth.drift_qkv(w, steps[-1], step=s_, seed=args.seed))
+    dev = [tuple(t.cuda() for t in x) for x in steps]
+    q, k, v = dev[0]
+    desc = mcs.desc_for(q)
+    dense = []
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    for i, (qs, ks, vs) in enumerate(dev):
+        o = torch.empty_like(qs)
+        mcs.anchor_dense_lse(qs, ks, vs, o, lse if i == 0 else None)
+        dense.append(o)
+    lse0 = lse.clone()
+
+    def rel_l1(a, b):
+        return float((a.float() - b.float()).abs().sum() / b.float().abs().sum())
+
+    ws = torch.empty(mcs.pddp_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+    perm_pddp = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    mcs.pddp_group(q, T, perm_pddp, ws)
+    perm_none = torch.arange(N, dtype=torch.int32, device="cuda").expand(B, H, N).contiguous()
+    sizes = torch.full((G,), float(T), device="cuda")
+    sizes[-1] = N - (G - 1) * T
+    mass = torch.empty((B, H, G, N), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    rows = []
+    for order, perm in (("pddp", perm_pddp), ("none", perm_none)):
+        idx_tok = torch.empty((B, H, G, K), dtype=torch.int32, device="cuda")
+        mcs.anchor_select_topk(q, k, lse0, perm, T, K, idx_tok, group_mass=mass)
+        full = (N // BLK) * BLK
+        bmass = mass[..., :full].reshape(B, H, G, N // BLK, BLK).sum(-1)
+        top = torch.topk(bmass, nb, dim=-1).indices.sort(dim=-1).values
+        idx_blk = (top.unsqueeze(-1) * BLK + torch.arange(BLK, device="cuda")).reshape(B, H, G, Kb).to(torch.int32)
+        for gran, idx, kk in (("token", idx_tok, K), ("block64", idx_blk.contiguous(), Kb)):
+            recall = float((mass.gather(-1, idx.long()).sum(-1) / sizes).mean())
+            mcs.sparse_apply(q, k, v, perm, T, idx, kk, None, out)
+            err_anchor = rel_l1(out, dense[0])
+            r = torch.empty_like(q)
+            mcs.residual(q, k, v, dense[0], perm, T, idx, kk, r)
+            errs = []
+            for (qs, ks, vs), od in zip(dev[1:], dense[1:]):
+                mcs.sparse_apply(qs, ks, vs, perm, T, idx, kk, r, out)
+                errs.append(rel_l1(out, od))
+            rows.append({"order": order, "granularity": gran, "keys": kk,
+                         "density_pct": round(100.0 * kk / N, 2), "recall": round(recall, 4),
+                         "rel_l1_sparse_anchor": round(err_anchor, 4),
+                         "rel_l1_reuse_with_R": [round(e, 4) for e in errs]})
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": w.name, "config": {"heads": H, "seqlen": N, "head_dim": d, "group_size": T,
+                                                     "density_pct": w.density_pct, "reuse_steps": len(dev) - 1,
+                                                     "drift": w.drift, "seed": args.seed},
+                      "variants": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -354,6 +430,8 @@ def main():
                     help="layer-stack workloads: R in pinned host memory with one-layer-ahead prefetch "
                          "(auto: on for voxel3d, whose offload the schedule is taken from; off for wanvideo, "
                          "whose 30 layers of R fit in HBM many times over)")
+    ap.add_argument("--variants", action="store_true",
+                    help="selection-variant diagnostics (query order x granularity) instead of the bench line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales the rocprofv3 byte counters)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH", "WRITE", "FETCH_COPY", "WRITE_COPY"),
@@ -381,6 +459,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.variants:
+        from sparse_attention_diffusion_pddp_amd import synth
+        w = synth.WORKLOADS[args.workload]
+        if args.density is not None:
+            w = w.with_density(args.density)
+        return run_variants(args, w)
     if args.workload in ("voxel3d", "wanvideo"):
         from sparse_attention_diffusion_pddp_amd import schedule, synth
         name, sched = (("voxel3d", schedule.HY3D) if args.workload == "voxel3d"
