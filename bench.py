@@ -156,7 +156,7 @@ def schedule_inputs(w, sched, seed):
     return (lambda step, layer: dev[which(step)]), dev
 
 
-def run_schedule(args, w, sched, offload=True):
+def run_schedule(args, w, sched, offload=True, offload_idx=False):
     """A whole layer stack over all denoising steps through StackRunner
     (appendix Table 9 schedules): dense warm-up steps and always-dense
     layers, anchors that (re)build groups, indices and R, reuse layers in
@@ -171,7 +171,7 @@ def run_schedule(args, w, sched, offload=True):
     torch.cuda.set_device(0)
     B, H, N, d, T, K = w.batch, w.heads, w.seqlen, w.head_dim, w.group_size, w.topk
     inputs, dev = schedule_inputs(w, sched, args.seed)
-    runner = schedule.StackRunner(sched, dev[0][0].shape, T, K, offload=offload)
+    runner = schedule.StackRunner(sched, dev[0][0].shape, T, K, offload=offload, offload_idx=offload_idx)
     runner.run(inputs)  # warm-up pass of the whole schedule
     torch.cuda.synchronize()
     ev = {}
@@ -179,9 +179,12 @@ def run_schedule(args, w, sched, offload=True):
     runner.run(inputs, events=ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the bare H2D copy of one layer's R from pinned memory, nothing else running
-    host = torch.empty(runner.r_bytes, dtype=torch.uint8, pin_memory=True)
-    devbuf = torch.empty(runner.r_bytes, dtype=torch.uint8, device="cuda")
+    # the bare H2D copy of one layer's offloaded bytes from pinned memory,
+    # nothing else running
+    bm_bytes = runner.bm_bytes if offload_idx else 0
+    moved = runner.r_bytes + bm_bytes
+    host = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+    devbuf = torch.empty(moved, dtype=torch.uint8, device="cuda")
     e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     devbuf.copy_(host, non_blocking=True)
     e[0].record()
@@ -197,6 +200,7 @@ def run_schedule(args, w, sched, offload=True):
         return (sum(xs) / len(xs) if xs else 0.0), len(xs)
 
     reuse_ms, n_reuse = avg("reuse")
+    decode_ms, _ = avg("decode")
     pf_ms, n_pf = avg("prefetch")
     anchor_ms, n_anchor = avg("anchor")
     pddp_ms, _ = avg("pddp")
@@ -235,7 +239,7 @@ def run_schedule(args, w, sched, offload=True):
                    "group_size": T, "density_pct": w.density_pct, "topk": K, "layers": sched.layers,
                    "denoise_steps": sched.steps, "warmup_steps": sched.warmup_steps,
                    "anchor_steps": anchor_steps, "dense_layers": list(sched.dense_layers),
-                   "offload": offload, "seed": args.seed},
+                   "offload": offload, "offload_idx": offload_idx, "seed": args.seed},
         "schedule_counts": {"dense": n_dense, "anchor": n_anchor, "reuse": n_reuse, "prefetch": n_pf,
                             "store": len(ev.get("store", []))},
         "anchor_step_ms": [round(step_ms[st - 1], 3) for st in anchor_steps],
@@ -249,11 +253,15 @@ def run_schedule(args, w, sched, offload=True):
         "denoise_ms": round(sum(step_ms), 1),
         "all_dense_denoise_ms": round(all_dense_ms, 1),
         "attention_speedup_vs_all_dense": round(all_dense_ms / sum(step_ms), 3),
-        "table8_row": {"V_MB": round(r_bytes / 1e6, 1), "V_MiB": round(r_bytes / 2**20, 1),
+        "table8_row": {"V_MB": round(moved / 1e6, 1), "V_MiB": round(moved / 2**20, 1),
+                       "R_MB": round(r_bytes / 1e6, 1),
+                       "idx_bitmap_MB": round(bm_bytes / 1e6, 1),
+                       "idx_int32_MB": round(B * H * runner.G * K * 4 / 1e6, 1),
                        "C_TFLOP": round(flops / 1e12, 3),
-                       "C_over_V": round(metrics.offload_ratio(flops / 1e12, r_bytes / 2**20)),
-                       "transfer_ms": round(h2d_ms, 3), "transfer_GBps": round(r_bytes / (h2d_ms * 1e-3) / 1e9, 1),
+                       "C_over_V": round(metrics.offload_ratio(flops / 1e12, moved / 2**20)),
+                       "transfer_ms": round(h2d_ms, 3), "transfer_GBps": round(moved / (h2d_ms * 1e-3) / 1e9, 1),
                        "prefetch_span_ms": round(pf_ms, 3),
+                       "decode_ms": round(decode_ms, 3),
                        "compute_ms": round(reuse_ms, 3),
                        "exposed_wait_ms_per_reuse_step": round(exposed, 3),
                        "hidden_per_layer": bool(h2d_ms <= reuse_ms),
@@ -430,6 +438,8 @@ def main():
                     help="layer-stack workloads: R in pinned host memory with one-layer-ahead prefetch "
                          "(auto: on for voxel3d, whose offload the schedule is taken from; off for wanvideo, "
                          "whose 30 layers of R fit in HBM many times over)")
+    ap.add_argument("--offload-idx", action="store_true",
+                    help="layer-stack workloads with offload: also offload the KV indices, as bitmaps")
     ap.add_argument("--variants", action="store_true",
                     help="selection-variant diagnostics (query order x granularity) instead of the bench line")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -473,7 +483,7 @@ def main():
         if args.density is not None:
             w = w.with_density(args.density)
         offload = args.offload == "on" or (args.offload == "auto" and args.workload == "voxel3d")
-        return run_schedule(args, w, sched, offload=offload)
+        return run_schedule(args, w, sched, offload=offload, offload_idx=offload and args.offload_idx)
     if args.workload == "wan720p":
         from sparse_attention_diffusion_pddp_amd import synth
         w = synth.WORKLOADS["wan720p"]

@@ -14,7 +14,8 @@
  *                       (mcs_residual)            walkthrough step 3
  * and a reuse step computes sparse attention over the cached indices with
  * fresh Q/K/V and adds R (mcs_sparse_apply)       walkthrough step 4.
- * R can be offloaded to pinned host memory and prefetched one layer ahead
+ * R, and the KV indices in bitmap form (mcs_kv_idx_encode / _decode), can
+ * be offloaded to pinned host memory and prefetched one layer ahead
  * (mcs_rcache_*)                                  walkthrough step 5; Table 8.
  *
  * Conventions shared by every call
@@ -163,6 +164,28 @@ mcs_status_t mcs_sparse_apply(const mcs_attn_desc_t *desc, const void *q, const 
                               const void *v, const int32_t *perm, int32_t group_size,
                               const int32_t *kv_idx, int32_t topk, const void *r, void *o,
                               mcs_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Compact KV indices for offload (research walkthrough page, method step 5;
+ * paper landing page, Table 8, which offloads the selected KV indices beside
+ * the residuals): one bit per key.
+ *   bitmap  uint32 [B][H][G][W], W = ceil(N/32); bit (j % 32) of word j / 32
+ *           of a row is set iff key j is in that row of kv_idx.
+ *   mcs_kv_idx_bitmap_bytes: B*H*G*W*4.
+ *   encode: kv_idx int32 [B][H][G][topk] -> bitmap. Entries outside [0, N)
+ *           are dropped, repeated entries collapse.
+ *   decode: bitmap -> kv_idx, ascending; each row must hold exactly topk set
+ *           bits (what encode makes from a list of distinct in-range keys):
+ *           with more, the first topk are written; with fewer, the tail of
+ *           the row is left as it was.
+ *   seqlen above 2^19 is MCS_ERR_UNSUPPORTED; kv_idx and bitmap must not
+ *   overlap. Both enqueue on `stream`.
+ * ------------------------------------------------------------------------ */
+mcs_status_t mcs_kv_idx_bitmap_bytes(const mcs_attn_desc_t *desc, int32_t group_size, size_t *bytes);
+mcs_status_t mcs_kv_idx_encode(const mcs_attn_desc_t *desc, int32_t group_size, const int32_t *kv_idx,
+                               int32_t topk, uint32_t *bitmap, mcs_stream_t stream);
+mcs_status_t mcs_kv_idx_decode(const mcs_attn_desc_t *desc, int32_t group_size, const uint32_t *bitmap,
+                               int32_t topk, int32_t *kv_idx, mcs_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Step 5: host offload of cached metadata with a one-layer-ahead prefetch

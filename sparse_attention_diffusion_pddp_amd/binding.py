@@ -34,6 +34,9 @@ SIGNATURES = [
     ("mcs_anchor_select_topk", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _sz, _p]),
     ("mcs_residual", _i32, [_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p]),
     ("mcs_sparse_apply", _i32, [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p]),
+    ("mcs_kv_idx_bitmap_bytes", _i32, [_p, _i32, ctypes.POINTER(_sz)]),
+    ("mcs_kv_idx_encode", _i32, [_p, _i32, _p, _i32, _p, _p]),
+    ("mcs_kv_idx_decode", _i32, [_p, _i32, _p, _i32, _p, _p]),
     ("mcs_rcache_create", _i32, [_i32, _sz, ctypes.POINTER(_p)]),
     ("mcs_rcache_store", _i32, [_p, _i32, _p, _p]),
     ("mcs_rcache_prefetch", _i32, [_p, _i32, _p]),
@@ -162,6 +165,27 @@ def sparse_apply(q, k, v, perm, group_size, kv_idx, topk, r, o, desc=None, strea
     desc = desc or desc_for(q)
     _check("mcs_sparse_apply", lib.mcs_sparse_apply(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(perm),
                                                     group_size, _ptr(kv_idx), topk, _ptr(r), _ptr(o), _stream(stream)))
+
+
+def kv_idx_bitmap_bytes(desc: Desc, group_size: int) -> int:
+    lib = load()
+    n = ctypes.c_size_t()
+    _check("mcs_kv_idx_bitmap_bytes", lib.mcs_kv_idx_bitmap_bytes(ctypes.byref(desc), group_size, ctypes.byref(n)))
+    return n.value
+
+
+def kv_idx_encode(desc: Desc, group_size, kv_idx, topk, bitmap, stream=None):
+    """kv_idx int32 [B][H][G][topk] -> bitmap uint32 [B][H][G][ceil(N/32)] (any 4-byte tensor)."""
+    lib = load()
+    _check("mcs_kv_idx_encode", lib.mcs_kv_idx_encode(ctypes.byref(desc), group_size, _ptr(kv_idx), topk,
+                                                      _ptr(bitmap), _stream(stream)))
+
+
+def kv_idx_decode(desc: Desc, group_size, bitmap, topk, kv_idx, stream=None):
+    """bitmap -> kv_idx, ascending (each row must hold exactly topk set bits)."""
+    lib = load()
+    _check("mcs_kv_idx_decode", lib.mcs_kv_idx_decode(ctypes.byref(desc), group_size, _ptr(bitmap), topk,
+                                                      _ptr(kv_idx), _stream(stream)))
 
 
 class RCache:

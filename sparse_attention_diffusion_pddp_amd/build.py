@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libmcsparse.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["mcs_api.cpp", "mcs_rcache.cpp", "mcs_attention.hip", "mcs_select.hip", "mcs_pddp.hip"]
+SOURCES = ["mcs_api.cpp", "mcs_rcache.cpp", "mcs_attention.hip", "mcs_select.hip", "mcs_pddp.hip",
+           "mcs_idxcode.hip"]
 
 # packed fp32 instructions stay off (-packed-fp32-ops): the compiler would
 # otherwise form v_pk_{add,mul,fma}_f32 from plain float code.

@@ -2,6 +2,7 @@
 // error reporting. Every check runs before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -282,6 +283,51 @@ mcs_status_t mcs_sparse_apply(const mcs_attn_desc_t *desc, const void *q, const 
   a.K = topk;
   return hip_status(mcs::launch_attention(mcs::kModeSparse, desc->head_dim, a, (hipStream_t)stream),
                     "mcs_sparse_apply");
+}
+
+mcs_status_t mcs_kv_idx_bitmap_bytes(const mcs_attn_desc_t *desc, int32_t group_size, size_t *bytes) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_group(group_size));
+  if (!bytes) return fail(MCS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = (size_t)desc->batch * desc->heads * groups_of(desc, group_size) * mcs::idx_bitmap_words(desc->seqlen) * 4;
+  return ok();
+}
+
+namespace {
+// the encoder builds one row's words in LDS (64 KB at most)
+constexpr int32_t kMaxBitmapKeys = 64 * 1024 * 8;
+
+mcs_status_t check_code_args(const mcs_attn_desc_t *desc, int32_t group_size, int32_t topk, const void *idx,
+                             const void *bitmap) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_group(group_size));
+  MCS_TRY(check_topk(desc, topk));
+  if (desc->seqlen > kMaxBitmapKeys)
+    return fail(MCS_ERR_UNSUPPORTED, "seqlen %d above the bitmap codec's %d keys", desc->seqlen, kMaxBitmapKeys);
+  MCS_TRY(check_ptr(idx, "kv_idx"));
+  MCS_TRY(check_ptr(bitmap, "bitmap"));
+  const int64_t rows = (int64_t)desc->batch * desc->heads * groups_of(desc, group_size);
+  if (overlaps(idx, bitmap, (int64_t)std::min<int64_t>(rows * topk * 4,
+                                                      rows * (int64_t)mcs::idx_bitmap_words(desc->seqlen) * 4)))
+    return fail(MCS_ERR_INVALID_ARGUMENT, "kv_idx and bitmap overlap");
+  return ok();
+}
+}  // namespace
+
+mcs_status_t mcs_kv_idx_encode(const mcs_attn_desc_t *desc, int32_t group_size, const int32_t *kv_idx,
+                               int32_t topk, uint32_t *bitmap, mcs_stream_t stream) {
+  MCS_TRY(check_code_args(desc, group_size, topk, kv_idx, bitmap));
+  const int64_t rows = (int64_t)desc->batch * desc->heads * groups_of(desc, group_size);
+  return hip_status(mcs::launch_idx_encode(kv_idx, rows, topk, desc->seqlen, bitmap, (hipStream_t)stream),
+                    "mcs_kv_idx_encode");
+}
+
+mcs_status_t mcs_kv_idx_decode(const mcs_attn_desc_t *desc, int32_t group_size, const uint32_t *bitmap,
+                               int32_t topk, int32_t *kv_idx, mcs_stream_t stream) {
+  MCS_TRY(check_code_args(desc, group_size, topk, kv_idx, bitmap));
+  const int64_t rows = (int64_t)desc->batch * desc->heads * groups_of(desc, group_size);
+  return hip_status(mcs::launch_idx_decode(bitmap, rows, topk, desc->seqlen, kv_idx, (hipStream_t)stream),
+                    "mcs_kv_idx_decode");
 }
 
 }  // extern "C"

@@ -39,6 +39,11 @@ struct SelectArgs {
 };
 hipError_t launch_select(int head_dim, const SelectArgs &a, hipStream_t s);
 
+// bitmap form of the KV indices: ceil(N/32) words per (b, h, g) row
+size_t idx_bitmap_words(int N);
+hipError_t launch_idx_encode(const int32_t *idx, int64_t rows, int K, int N, uint32_t *bitmap, hipStream_t s);
+hipError_t launch_idx_decode(const uint32_t *bitmap, int64_t rows, int K, int N, int32_t *idx, hipStream_t s);
+
 size_t pddp_workspace_bytes(int B, int H, int N, int D, int T);
 hipError_t run_pddp(const uint16_t *q, int64_t sb, int64_t sn, int64_t sh, int B, int H, int N,
                     int D, int T, int power_iters, int32_t *perm, void *ws, size_t ws_bytes,

@@ -17,7 +17,9 @@ anyway). A layer that is not always dense and has no anchor yet runs dense.
 ``StackRunner`` executes a plan on one GPU through libmcsparse, keeping each
 sparse layer's groups and indices on the device and its R in an offload
 cache (pinned host memory, two device slots, one-layer-ahead prefetch on a
-side stream).
+side stream). With ``offload_idx`` the indices are offloaded too, as
+bitmaps (one bit per key), and decoded into one shared device buffer just
+before each reuse call (paper landing page, Table 8 offloads both).
 """
 from __future__ import annotations
 
@@ -79,15 +81,23 @@ class StackRunner:
     ``side`` one layer ahead of its reuse, acquired on the compute stream.
     """
 
-    def __init__(self, sched: Schedule, shape, group_size, topk, power_iters=16, offload=True):
+    def __init__(self, sched: Schedule, shape, group_size, topk, power_iters=16, offload=True, offload_idx=False):
         B, N, H, d = shape
         self.s, self.T, self.K = sched, group_size, topk
         self.B, self.N, self.H, self.d = B, N, H, d
         self.G = -(-N // group_size)
         self.sparse_layers = [l for l in range(sched.layers) if l not in sched.dense_layers]
+        if offload_idx and not offload:
+            raise ValueError("offload_idx needs offload")
+        self.offload_idx = offload_idx
         dev = "cuda"
         self.perm = {l: torch.empty((B, H, N), dtype=torch.int32, device=dev) for l in self.sparse_layers}
-        self.idx = {l: torch.empty((B, H, self.G, topk), dtype=torch.int32, device=dev) for l in self.sparse_layers}
+        idx_shape = (B, H, self.G, topk)
+        if offload_idx:
+            shared = torch.empty(idx_shape, dtype=torch.int32, device=dev)
+            self.idx = {l: shared for l in self.sparse_layers}
+        else:
+            self.idx = {l: torch.empty(idx_shape, dtype=torch.int32, device=dev) for l in self.sparse_layers}
         self.o = torch.empty(shape, dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         self.r = torch.empty(shape, dtype=torch.bfloat16, device=dev)
@@ -102,6 +112,13 @@ class StackRunner:
         self.offload = offload
         self.r_bytes = self.r.numel() * self.r.element_size()
         self.cache = mcs.RCache(sched.layers, self.r_bytes) if offload else None
+        self.icache = None
+        if offload_idx:
+            self.bm_bytes = mcs.kv_idx_bitmap_bytes(self.desc, group_size)
+            padded = -(-self.bm_bytes // 256) * 256
+            self.bm_stage = [torch.zeros(padded // 4, dtype=torch.int32, device=dev) for _ in range(2)]
+            self.icache = mcs.RCache(sched.layers, padded)
+            self.bm_like = self.bm_stage[0]
         self.r_dev = {} if offload else {l: torch.empty(shape, dtype=torch.bfloat16, device=dev)
                                          for l in self.sparse_layers}
         self.side = torch.cuda.Stream()
@@ -111,6 +128,9 @@ class StackRunner:
         if self.cache is not None:
             self.cache.close()
             self.cache = None
+        if self.icache is not None:
+            self.icache.close()
+            self.icache = None
 
     def _r_view(self, ptr):
         """The R slot returned by the cache, as the caller's bf16 tensor layout."""
@@ -159,12 +179,17 @@ class StackRunner:
                     else:
                         rdst = self.r_dev[layer]
                     mcs.residual(q, k, v, self.o, self.perm[layer], self.T, self.idx[layer], self.K, rdst)
+                    if self.offload_idx:
+                        bdst = self.bm_stage[buf]
+                        mcs.kv_idx_encode(self.desc, self.T, self.idx[layer], self.K, bdst)
                     _push(events, "anchor", e0, _ev(rec))
                     if self.offload:
                         # D2H on the side stream, after the residual
                         self.side.wait_stream(compute)
                         e1 = _ev(rec, self.side)
                         self.cache.store(layer, rdst, self.side)
+                        if self.offload_idx:
+                            self.icache.store(layer, bdst, self.side)
                         _push(events, "store", e1, _ev(rec, self.side))
                         done = torch.cuda.Event()
                         done.record(self.side)
@@ -172,6 +197,12 @@ class StackRunner:
                 else:
                     if self.offload:
                         ptr = self.cache.acquire(layer, compute)
+                        if self.offload_idx:
+                            bptr = self.icache.acquire(layer, compute)
+                            e1 = _ev(rec)
+                            mcs.kv_idx_decode(self.desc, self.T, _DevicePtr(bptr, self.bm_like), self.K,
+                                              self.idx[layer])
+                            _push(events, "decode", e1, _ev(rec))
                         nxt = [l for l in reuse_layers if l > layer]
                         if nxt:
                             self._prefetch(nxt[0], events)
@@ -189,6 +220,8 @@ class StackRunner:
         rec = events is not None
         e0 = _ev(rec, self.side)
         self.cache.prefetch(layer, self.side)
+        if self.icache is not None:
+            self.icache.prefetch(layer, self.side)
         _push(events, "prefetch", e0, _ev(rec, self.side))
 
 

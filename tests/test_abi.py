@@ -25,7 +25,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(s[0] for s in B.SIGNATURES) == names
@@ -88,3 +88,21 @@ def test_rcache_argument_checks(lib):
     assert lib.mcs_rcache_create(2, 1024, None) == 1
     assert lib.mcs_rcache_store(None, 0, FAKE, None) == 1
     assert lib.mcs_rcache_destroy(None) == 1
+
+
+def test_kv_idx_codec_argument_checks(lib):
+    d = desc(H=12, N=32760)
+    n = ctypes.c_size_t()
+    assert lib.mcs_kv_idx_bitmap_bytes(ctypes.byref(d), 128, ctypes.byref(n)) == 0
+    assert n.value == 12 * 256 * 1024 * 4  # ceil(32760 / 32) = 1024 words per group
+    assert lib.mcs_kv_idx_bitmap_bytes(ctypes.byref(d), 96, ctypes.byref(n)) == 2
+    other = ctypes.c_void_p((1 << 30))
+    assert lib.mcs_kv_idx_encode(ctypes.byref(d), 128, FAKE, 0, other, None) == 1
+    assert lib.mcs_kv_idx_decode(ctypes.byref(d), 128, other, 32761, FAKE, None) == 1
+    assert lib.mcs_kv_idx_encode(ctypes.byref(d), 128, FAKE, 10, FAKE, None) == 1
+    assert b"overlap" in lib.mcs_last_error()
+    assert lib.mcs_kv_idx_encode(ctypes.byref(d), 128, None, 10, other, None) == 1
+    mis = ctypes.c_void_p((1 << 30) + 2)
+    assert lib.mcs_kv_idx_decode(ctypes.byref(d), 128, mis, 10, FAKE, None) == 1
+    big = desc(H=1, N=(1 << 19) + 1)
+    assert lib.mcs_kv_idx_encode(ctypes.byref(big), 128, FAKE, 10, other, None) == 2

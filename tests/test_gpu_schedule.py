@@ -66,7 +66,8 @@ def test_refreshed_anchor_reuses_the_new_metadata(lib):
     """Two anchors (Table 9's refresh): the reuse layers after the second
     anchor use the groups, indices and R computed from that anchor's inputs,
     those before it the first anchor's; warm-up steps and layer 0 stay dense.
-    Offloaded and device-resident R agree bitwise."""
+    Metadata kept on the device, R offloaded, and R plus the indices (as
+    bitmaps) offloaded all give the same outputs bitwise."""
     sched = S.Schedule(steps=5, layers=3, dense_layers=(0,), warmup_steps=1, anchor_steps=(2, 4))
     w = synth.small_workload(640, heads=2, head_dim=128, group_size=128, density_pct=20)
     per_step = {1: synth.make_qkv(w, seed=33)}
@@ -78,16 +79,21 @@ def test_refreshed_anchor_reuses_the_new_metadata(lib):
     c = S.counts(S.plan(sched))
     assert c == {"dense": 3 + 4, "anchor": 4, "reuse": 4}
     outs = {}
-    for offload in (True, False):
-        r = S.StackRunner(sched, shape, w.group_size, w.topk, offload=offload)
+    # R on the device; R offloaded; R and the indices (as bitmaps) offloaded
+    for mode in ((False, False), (True, False), (True, True)):
+        r = S.StackRunner(sched, shape, w.group_size, w.topk, offload=mode[0], offload_idx=mode[1])
         ev, out = {}, {}
         r.run(inputs, events=ev, outputs=out)
         torch.cuda.synchronize()
         assert len(ev["anchor"]) == c["anchor"] and len(ev["reuse"]) == c["reuse"] and len(ev["dense"]) == c["dense"]
-        outs[offload] = out
+        if mode[1]:
+            assert len(ev["decode"]) == c["reuse"]
+        outs[mode] = out
         r.close()
-    for key in outs[True]:
-        assert torch.equal(outs[True][key], outs[False][key]), key
+    for mode in ((True, False), (True, True)):
+        for key in outs[(False, False)]:
+            assert torch.equal(outs[mode][key], outs[(False, False)][key]), (mode, key)
+    outs[True] = outs[(True, True)]
     scale = 1.0 / math.sqrt(w.head_dim)
     h = 1
     for anchor_step, reuse_step in ((2, 3), (4, 5)):
