@@ -134,6 +134,17 @@ def cpu_baseline(w, seconds: float, seed: int):
                       f"{elapsed:.1f} s of oracle time, float64 numpy"}
 
 
+def input_set(step, anchors):
+    """Which activation set a denoising step uses (see schedule_inputs):
+    0 up to the first anchor, then one drifted set between anchors and one at
+    each later anchor."""
+    anchors = sorted(anchors)
+    if step <= anchors[0]:
+        return 0
+    n = sum(1 for a in anchors if a <= step)
+    return 2 * n - 2 if step in anchors else 2 * n - 1
+
+
 def schedule_inputs(w, sched, seed):
     """Activations for a layer-stack run: the first anchor's Q/K/V (also used
     by the dense warm-up steps before it), then one drifted set between
@@ -146,14 +157,7 @@ def schedule_inputs(w, sched, seed):
     for i in range(1, 2 * len(anchors)):
         sets.append(synth.drift_qkv(w, sets[-1], step=i, seed=seed))
     dev = [tuple(t.cuda() for t in x) for x in sets]
-
-    def which(step):
-        if step <= anchors[0]:
-            return 0
-        n = sum(1 for a in anchors if a <= step)
-        return 2 * n - 2 if step in anchors else 2 * n - 1
-
-    return (lambda step, layer: dev[which(step)]), dev
+    return (lambda step, layer: dev[input_set(step, anchors)]), dev
 
 
 def run_schedule(args, w, sched, offload=True, offload_idx=False):
