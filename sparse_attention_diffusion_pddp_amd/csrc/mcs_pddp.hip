@@ -9,19 +9,34 @@
 // level stably partitions every active node's range in place, which keeps
 // every node (and finally every group) in ascending token order.
 //
-// Every level runs five kernels over all heads and nodes at once:
-//   mean     per chunk of a node: sum of q (float64)           -> partials
-//   cov      per chunk: sum of (q-mu)(q-mu)^T on the fp64 MFMA
-//            (v_mfma_f64_16x16x4_f64, upper-triangle tiles)      -> partials
+// Second moments are additive, so a split's children need only one pass:
+// the moments of the left child (never larger than the right one) are
+// accumulated from its tokens and the right child's are the parent's minus
+// the left's. Every moment is taken about one fixed point per head, the
+// head's token 0 (c), so that x - c is exact and the moments stay small for
+// data with a common offset: s = sum (x - c), S = sum (x - c)(x - c)^T, and a
+// node's covariance is S/n - m m^T with m = s/n, its mean c + m.
+//
+// Per level, over all heads and nodes at once:
+//   moment   per chunk of a unit (a range whose moments are accumulated):
+//            s and the upper-triangle 16x16 tiles of S on the fp64 MFMA
+//            (v_mfma_f64_16x16x4_f64)                            -> partials
 //            (its accumulator: lane l, register i holds row l/16 + 4i,
 //            column l % 16; operands: lane l holds row/col l % 16, k = l/16)
-//   power    per node: add the partials in chunk order (fixed, no atomics),
-//            power iteration from e_{argmax diag}, orientation    -> mu, u
-//   project  per chunk: p_i = (q_i - mu) . u in float64
+//   reduce   (levels whose units span more than 4 chunks) partials of a
+//            unit added in chunk order, sliced over many blocks
+//   power    per node: its moments (unit, or parent minus unit), kept for
+//            the next level when its right child is split again; the
+//            covariance, power iteration from e_{argmax diag}, orientation
+//            -> mu, u
+//   project  per chunk of a node: p_i = (q_i - mu) . u in float64
 //   split    per node: radix select of the floor(G_S/2)*T-th smallest
 //            (p, position) and a stable partition of the node's range.
-// Decisions are taken on float64 values so the split does not hinge on
-// fp32 rounding.
+// All sums run in a fixed order, so the result is bitwise reproducible, and
+// decisions are taken on float64 values so the split does not hinge on fp32
+// rounding. Level 0 needs neither the plan nor perm (its one unit is the
+// whole sequence in token order): its moment kernel writes the identity perm
+// and one extra block builds the plan tables meanwhile.
 #include <vector>
 
 #include "mcs_common.hpp"
@@ -32,114 +47,162 @@ namespace mcs {
 
 namespace {
 
-constexpr int kChunk = 1024;       // tokens per chunk of the per-chunk kernels
+constexpr int kChunk0 = 512;     // tokens per moment chunk at level 0
+constexpr int kChunk = 256;      // tokens per moment chunk below level 0
+constexpr int kPChunk = 1024;    // tokens per projection chunk
+constexpr int kDirectChunks = 4; // a unit of at most this many chunks is summed by the power kernel
 constexpr int kMaxLevels = 40;
 constexpr int kSplitThreads = 512;
 
 struct PLevel {
-  int node0, nnodes, chunk0, nchunks;
+  int node0, nnodes;     // nodes (more than T tokens) split at this level
+  int unit0, nunits;     // units whose moments this level accumulates
+  int mchunk0, nmchunks; // moment chunks (over units)
+  int pchunk0, npchunks; // projection chunks (over nodes)
+  int reduced;           // 1: a reduce pass adds the units' partials
 };
 struct PNode {
-  int off, n, nl, chunk0, nchunks;  // chunk0: level-local index of its first chunk
+  int off, n, nl;
+  int unit;      // level-local unit: the node's own range, or its left sibling's
+  int derived;   // 1: moments = parent's - unit's (a right child)
+  int kid_unit;  // next-level unit of its children when the right child is split again, else -1
+};
+struct PUnit {
+  int off, n, chunk0, nchunks;  // chunk0: level-local index of its first moment chunk
 };
 struct PChunk {
-  int node, off, len;  // node: level-local node index; off: absolute position
+  int owner, off, len;  // owner: level-local unit (moment) or node (projection)
 };
 
 struct PlanCounts {
-  int levels, nodes, chunks, max_nodes, max_chunks;
+  int levels, nodes, units, mchunks, pchunks;
+  int max_nodes, max_units, max_runits, max_mchunks, max_pchunks;
 };
 
-// Builds the level / node / chunk tables. `nd` must hold at least 2*G nodes;
-// `lv` and `ch` may be null to only count.
-__host__ __device__ PlanCounts plan_tree(int N, int T, PLevel *lv, PNode *nd, PChunk *ch) {
-  PlanCounts pc{0, 0, 0, 0, 0};
-  if (N <= T) return pc;
+// Builds the level / node / unit / chunk tables. `nd` and `un` must hold at
+// least 2*G + 2 entries; `lv`, `mc` and `pc` may be null to only count.
+__host__ __device__ PlanCounts plan_tree(int N, int T, PLevel *lv, PNode *nd, PUnit *un, PChunk *mc,
+                                         PChunk *pc) {
+  PlanCounts k{};
+  if (N <= T) return k;
   // active nodes (more than T tokens) are appended level by level, so the
-  // nodes of one level are contiguous; level 0 is the root
-  nd[0] = PNode{0, N, 0, 0, 0};
-  int lvl_begin = 0, lvl_end = 1;
-  while (lvl_begin < lvl_end) {
-    int level_chunks = 0;
-    int next_end = lvl_end;
-    for (int i = lvl_begin; i < lvl_end; ++i) {
+  // nodes of one level are contiguous; so are the units; level 0 is the root
+  nd[0] = PNode{0, N, 0, 0, 0, -1};
+  un[0] = PUnit{0, N, 0, 0};
+  int lb = 0, le = 1, ub = 0, ue = 1;
+  while (lb < le) {
+    const int cs = k.levels == 0 ? kChunk0 : kChunk;
+    int nm = 0, most = 0;
+    for (int u = ub; u < ue; ++u) {
+      PUnit x = un[u];
+      x.chunk0 = nm;
+      x.nchunks = (x.n + cs - 1) / cs;
+      if (mc)
+        for (int c = 0; c < x.nchunks; ++c) {
+          const int rest = x.n - c * cs;
+          mc[k.mchunks + nm + c] = PChunk{u - ub, x.off + c * cs, rest < cs ? rest : cs};
+        }
+      nm += x.nchunks;
+      most = most > x.nchunks ? most : x.nchunks;
+      un[u] = x;
+    }
+    int np = 0, nle = le, nue = ue;
+    for (int i = lb; i < le; ++i) {
       PNode x = nd[i];
       const int G = (x.n + T - 1) / T;
       x.nl = (G / 2) * T;
-      x.chunk0 = level_chunks;
-      x.nchunks = (x.n + kChunk - 1) / kChunk;
-      for (int c = 0; c < x.nchunks; ++c) {
-        const int rest = x.n - c * kChunk;
-        if (ch) ch[pc.chunks + level_chunks + c] = PChunk{i - lvl_begin, x.off + c * kChunk,
-                                                          rest < kChunk ? rest : kChunk};
+      const int nr = x.n - x.nl;  // nr >= nl: the right child is the larger
+      const int npc = (x.n + kPChunk - 1) / kPChunk;
+      if (pc)
+        for (int c = 0; c < npc; ++c) {
+          const int rest = x.n - c * kPChunk;
+          pc[k.pchunks + np + c] = PChunk{i - lb, x.off + c * kPChunk, rest < kPChunk ? rest : kPChunk};
+        }
+      np += npc;
+      x.kid_unit = -1;
+      if (nr > T) {
+        x.kid_unit = nue - ue;
+        un[nue++] = PUnit{x.off, x.nl, 0, 0};
+        if (x.nl > T) nd[nle++] = PNode{x.off, x.nl, 0, x.kid_unit, 0, -1};
+        nd[nle++] = PNode{x.off + x.nl, nr, 0, x.kid_unit, 1, -1};
       }
-      level_chunks += x.nchunks;
       nd[i] = x;
-      const int nr = x.n - x.nl;
-      if (x.nl > T) nd[next_end++] = PNode{x.off, x.nl, 0, 0, 0};
-      if (nr > T) nd[next_end++] = PNode{x.off + x.nl, nr, 0, 0, 0};
     }
-    if (lv) lv[pc.levels] = PLevel{lvl_begin, lvl_end - lvl_begin, pc.chunks, level_chunks};
-    const int nn = lvl_end - lvl_begin;
-    pc.max_nodes = pc.max_nodes > nn ? pc.max_nodes : nn;
-    pc.max_chunks = pc.max_chunks > level_chunks ? pc.max_chunks : level_chunks;
-    pc.chunks += level_chunks;
-    pc.levels++;
-    lvl_begin = lvl_end;
-    lvl_end = next_end;
+    const int red = most > kDirectChunks ? 1 : 0;
+    if (lv) lv[k.levels] = PLevel{lb, le - lb, ub, ue - ub, k.mchunks, nm, k.pchunks, np, red};
+    const int nn = le - lb, nu = ue - ub;
+    k.max_nodes = k.max_nodes > nn ? k.max_nodes : nn;
+    k.max_units = k.max_units > nu ? k.max_units : nu;
+    if (red) k.max_runits = k.max_runits > nu ? k.max_runits : nu;
+    k.max_mchunks = k.max_mchunks > nm ? k.max_mchunks : nm;
+    k.max_pchunks = k.max_pchunks > np ? k.max_pchunks : np;
+    k.mchunks += nm;
+    k.pchunks += np;
+    k.levels++;
+    lb = le;
+    le = nle;
+    ub = ue;
+    ue = nue;
   }
-  pc.nodes = lvl_end;
-  return pc;
+  k.nodes = le;
+  k.units = ue;
+  return k;
 }
 
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// doubles per moment block: the upper-triangle tiles of S, then s
+constexpr int moment_doubles(int D) { return (D / 16) * (D / 16 + 1) / 2 * 256 + D; }
+
 struct WsLayout {
-  size_t levels, nodes, chunks, mean_part, cov_part, mu, dir, proj, tmp, total;
+  size_t levels, nodes, units, mchunks, pchunks, part, ured, nodem, mu, dir, proj, tmp, total;
 };
 
 WsLayout ws_layout(const PlanCounts &pc, int BH, int N, int D) {
   WsLayout w{};
+  const size_t MB = (size_t)moment_doubles(D);
+  auto at_least1 = [](int x) { return (size_t)(x > 0 ? x : 1); };
   size_t o = 0;
   w.levels = o; o = align_up(o + sizeof(PLevel) * kMaxLevels);
-  w.nodes = o; o = align_up(o + sizeof(PNode) * (size_t)(pc.nodes > 0 ? pc.nodes : 1));
-  w.chunks = o; o = align_up(o + sizeof(PChunk) * (size_t)(pc.chunks > 0 ? pc.chunks : 1));
-  w.mean_part = o; o = align_up(o + sizeof(double) * (size_t)BH * pc.max_chunks * D);
-  w.cov_part = o; o = align_up(o + sizeof(double) * (size_t)BH * pc.max_chunks * D * D);
-  w.mu = o; o = align_up(o + sizeof(double) * (size_t)BH * pc.max_nodes * D);
-  w.dir = o; o = align_up(o + sizeof(double) * (size_t)BH * pc.max_nodes * D);
+  w.nodes = o; o = align_up(o + sizeof(PNode) * at_least1(pc.nodes));
+  w.units = o; o = align_up(o + sizeof(PUnit) * at_least1(pc.units));
+  w.mchunks = o; o = align_up(o + sizeof(PChunk) * at_least1(pc.mchunks));
+  w.pchunks = o; o = align_up(o + sizeof(PChunk) * at_least1(pc.pchunks));
+  w.part = o; o = align_up(o + sizeof(double) * (size_t)BH * at_least1(pc.max_mchunks) * MB);
+  w.ured = o; o = align_up(o + sizeof(double) * (size_t)BH * at_least1(pc.max_runits) * MB);
+  w.nodem = o; o = align_up(o + sizeof(double) * 2 * (size_t)BH * at_least1(pc.max_units) * MB);
+  w.mu = o; o = align_up(o + sizeof(double) * (size_t)BH * at_least1(pc.max_nodes) * D);
+  w.dir = o; o = align_up(o + sizeof(double) * (size_t)BH * at_least1(pc.max_nodes) * D);
   w.proj = o; o = align_up(o + sizeof(double) * (size_t)BH * N);
   w.tmp = o; o = align_up(o + sizeof(int32_t) * (size_t)BH * N);
   w.total = o;
   return w;
 }
 
-// Host-side plan with real arrays (the counting needs the node ranges).
-PlanCounts host_plan(int N, int T) {
-  if (N <= T) return PlanCounts{0, 0, 0, 0, 0};
+// Host-side plan with real node / unit arrays (counting needs the ranges).
+PlanCounts host_plan(int N, int T, PLevel *lv) {
+  if (N <= T) return PlanCounts{};
   const int G = (N + T - 1) / T;
   std::vector<PNode> nd(2 * G + 2);
-  return plan_tree(N, T, nullptr, nd.data(), nullptr);
+  std::vector<PUnit> un(2 * G + 2);
+  return plan_tree(N, T, lv, nd.data(), un.data(), nullptr, nullptr);
 }
 
 struct PddpArgs {
   const uint16_t *q;
   int64_t sb, sn, sh;
-  int B, H, N;
+  int B, H, N, T;
   int32_t *perm;
-  const PLevel *levels;
-  const PNode *nodes;
-  const PChunk *chunks;
-  double *mean_part, *cov_part, *mu, *dir, *proj;
+  PLevel *levels;
+  PNode *nodes;
+  PUnit *units;
+  PChunk *mchunks, *pchunks;
+  double *part, *ured, *nodem, *mu, *dir, *proj;
   int32_t *tmp;
-  int max_chunks, max_nodes;
+  int max_mchunks, max_runits, max_units, max_nodes;
   int level;
   int power_iters;
 };
-
-__global__ void plan_kernel(int N, int T, PLevel *lv, PNode *nd, PChunk *ch) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) plan_tree(N, T, lv, nd, ch);
-}
 
 __global__ void init_perm_kernel(int32_t *perm, int N, int64_t total) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -151,97 +214,89 @@ __device__ __forceinline__ const uint16_t *head_q(const PddpArgs &a, int bh) {
   return a.q + (int64_t)b * a.sb + (int64_t)h * a.sh;
 }
 
-// ---- mean partials: grid (nchunks, BH), 256 threads -------------------------
-template <int D>
-__global__ __launch_bounds__(256) void mean_kernel(PddpArgs a) {
-  constexpr int CH = D / 8;       // 16-byte chunks per row
-  constexpr int TL = 256 / CH;    // token lanes
-  __shared__ double red[TL][D + 1];
-  const PLevel L = a.levels[a.level];
-  const int bh = blockIdx.y;
-  const PChunk c = a.chunks[L.chunk0 + blockIdx.x];
+// ---- moment partials: grid (chunks [+1 at level 0], BH), 256 threads ----------
+// Tokens are staged through LDS as float64 (x - c), SUB at a time, the next
+// SUB rows already loaded into registers while the MFMAs run on these.
+template <int D, bool L0>
+__global__ __launch_bounds__(256) void moment_kernel(PddpArgs a) {
+  constexpr int NB = D / 16;                 // 16-wide dim blocks
+  constexpr int NT = NB * (NB + 1) / 2;      // upper-triangle tiles
+  constexpr int TPW = (NT + 3) / 4;          // tiles per wave (at most)
+  constexpr int MB = moment_doubles(D);
+  constexpr int SUB = 32;                    // tokens staged per step
+  constexpr int XS = D + 1;                  // LDS row stride (doubles)
+  constexpr int CH = D / 8;                  // 16-byte pieces per row
+  constexpr int TL = 256 / CH;               // token lanes
+  constexpr int RPT = SUB / TL;              // staged rows per thread
+  static_assert(RPT >= 1 && SUB % TL == 0 && TL <= SUB, "staging shape");
+  __shared__ double X[SUB * XS];
+
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int32_t *cur = a.perm + (int64_t)bh * a.N;
+  int off, len;
+  if (L0) {
+    const int nch = (a.N + kChunk0 - 1) / kChunk0;
+    if ((int)blockIdx.x == nch) {
+      if (bh == 0 && tid == 0) plan_tree(a.N, a.T, a.levels, a.nodes, a.units, a.mchunks, a.pchunks);
+      return;
+    }
+    off = blockIdx.x * kChunk0;
+    len = a.N - off < kChunk0 ? a.N - off : kChunk0;
+    for (int i = tid; i < len; i += 256) cur[off + i] = off + i;
+  } else {
+    const PChunk c = a.mchunks[a.levels[a.level].mchunk0 + blockIdx.x];
+    off = c.off;
+    len = c.len;
+  }
   const uint16_t *qh = head_q(a, bh);
-  const int32_t *cur = a.perm + (int64_t)bh * a.N;
-  const int col = threadIdx.x % CH, tl = threadIdx.x / CH;
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int i = tl; i < c.len; i += TL) {
-    const int tok = cur[c.off + i];
-    const u32x4 v = *(const u32x4 *)(qh + (int64_t)tok * a.sn + col * 8);
+  const int col = tid % CH, tl = tid / CH;
+
+  double cv[8];
+  {
+    const u32x4 v = *(const u32x4 *)(qh + col * 8);  // token 0 of the head
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      acc[2 * m] += (double)bf16_to_f32(v[m] & 0xffffu);
-      acc[2 * m + 1] += (double)bf16_to_f32(v[m] >> 16);
+      cv[2 * m] = (double)bf16_to_f32(v[m] & 0xffffu);
+      cv[2 * m + 1] = (double)bf16_to_f32(v[m] >> 16);
     }
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red[tl][col * 8 + e] = acc[e];
-  __syncthreads();
-  if (threadIdx.x < D) {
-    double s = 0.0;
-    for (int t = 0; t < TL; ++t) s += red[t][threadIdx.x];
-    a.mean_part[((int64_t)bh * a.max_chunks + blockIdx.x) * D + threadIdx.x] = s;
-  }
-}
-
-// ---- covariance partials: grid (nchunks, BH), 256 threads ------------------
-template <int D>
-__global__ __launch_bounds__(256) void cov_kernel(PddpArgs a) {
-  constexpr int NB = D / 16;                 // 16-wide dim blocks
-  constexpr int NTILES = NB * (NB + 1) / 2;  // upper-triangle tiles
-  constexpr int TPW = (NTILES + 3) / 4;      // tiles per wave (at most)
-  constexpr int SUB = 64;                    // tokens staged per step
-  constexpr int XS = D + 1;                  // LDS row stride (doubles)
-  constexpr int CH = D / 8;
-  constexpr int TL = 256 / CH;
-  __shared__ double X[SUB * XS];
-  __shared__ double mu_s[D];
-
-  const PLevel L = a.levels[a.level];
-  const int bh = blockIdx.y;
-  const PChunk c = a.chunks[L.chunk0 + blockIdx.x];
-  const PNode nd = a.nodes[L.node0 + c.node];
-  const uint16_t *qh = head_q(a, bh);
-  const int32_t *cur = a.perm + (int64_t)bh * a.N;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  if (tid < D) {
-    double s = 0.0;
-    const double *mp = a.mean_part + ((int64_t)bh * a.max_chunks + nd.chunk0) * D + tid;
-    for (int k = 0; k < nd.nchunks; ++k) s += mp[(int64_t)k * D];
-    mu_s[tid] = s / (double)nd.n;
-  }
-  __syncthreads();
-
-  // wave w owns the upper-triangle tiles t with t % 4 == w (t enumerates
-  // (bi, bj), bi <= bj, row-major); acc[t / 4] is its accumulator
+  double sx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   f64x4 acc[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) acc[k] = f64x4{0, 0, 0, 0};
 
-  const int col = tid % CH, tl = tid / CH;
-  double muc[8];
+  u32x4 pre[RPT];
+  bool ok[RPT];
+  auto fetch = [&](int base) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) muc[e] = mu_s[col * 8 + e];
-
-  for (int base = 0; base < c.len; base += SUB) {
-    // stage (q - mu) for SUB tokens; rows past the chunk are zero
-    for (int r = tl; r < SUB; r += TL) {
-      double x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (base + r < c.len) {
-        const int tok = cur[c.off + base + r];
-        const u32x4 v = *(const u32x4 *)(qh + (int64_t)tok * a.sn + col * 8);
+    for (int r = 0; r < RPT; ++r) {
+      const int i = base + tl + TL * r;
+      ok[r] = i < len;
+      const int tok = L0 ? off + (ok[r] ? i : 0) : cur[off + (ok[r] ? i : 0)];
+      pre[r] = *(const u32x4 *)(qh + (int64_t)tok * a.sn + col * 8);
+    }
+  };
+  fetch(0);
+  for (int base = 0; base < len; base += SUB) {
+    // stage x - c for SUB tokens; rows past the chunk are zero
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          x[2 * m] = (double)bf16_to_f32(v[m] & 0xffffu) - muc[2 * m];
-          x[2 * m + 1] = (double)bf16_to_f32(v[m] >> 16) - muc[2 * m + 1];
-        }
+    for (int r = 0; r < RPT; ++r) {
+      double x[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        x[2 * m] = ok[r] ? (double)bf16_to_f32(pre[r][m] & 0xffffu) - cv[2 * m] : 0.0;
+        x[2 * m + 1] = ok[r] ? (double)bf16_to_f32(pre[r][m] >> 16) - cv[2 * m + 1] : 0.0;
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) X[r * XS + col * 8 + e] = x[e];
+      for (int e = 0; e < 8; ++e) {
+        sx[e] += x[e];
+        X[(tl + TL * r) * XS + col * 8 + e] = x[e];
+      }
     }
     __syncthreads();
-    const int steps = (c.len - base) < SUB ? ((c.len - base + 3) / 4) : SUB / 4;
+    if (base + SUB < len) fetch(base + SUB);
+    const int steps = (len - base) < SUB ? ((len - base + 3) / 4) : SUB / 4;
     for (int s = 0; s < steps; ++s) {
       const int row = 4 * s + (lane >> 4);
       double fr[NB];
@@ -259,22 +314,53 @@ __global__ __launch_bounds__(256) void cov_kernel(PddpArgs a) {
     }
     __syncthreads();
   }
-  double *out = a.cov_part + ((int64_t)bh * a.max_chunks + blockIdx.x) * D * D;
+  // s: add the token lanes' sums in lane order
+#pragma unroll
+  for (int e = 0; e < 8; ++e) X[tl * XS + col * 8 + e] = sx[e];
+  __syncthreads();
+  double *out = a.part + ((int64_t)bh * a.max_mchunks + blockIdx.x) * MB;
+  if (tid < D) {
+    double s = 0.0;
+    for (int t = 0; t < TL; ++t) s += X[t * XS + tid];
+    out[NT * 256 + tid] = s;
+  }
   int t = 0;
 #pragma unroll
   for (int bi = 0; bi < NB; ++bi) {
 #pragma unroll
     for (int bj = bi; bj < NB; ++bj, ++t) {
       if ((t & 3) == wave) {
-        const int colj = 16 * bj + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rowi = 16 * bi + (lane >> 4) + 4 * i;  // f64 MFMA: row = lane/16 + 4*i
-          out[(int64_t)rowi * D + colj] = acc[t >> 2][i];
-        }
+        for (int i = 0; i < 4; ++i)  // f64 MFMA: row = lane/16 + 4*i, column = lane % 16
+          out[t * 256 + ((lane >> 4) + 4 * i) * 16 + (lane & 15)] = acc[t >> 2][i];
       }
     }
   }
+}
+
+// ---- unit moments: grid (units * slices, BH), 256 threads -------------------
+// Entry e of a unit's moments = its chunks' partials added in chunk order.
+template <int D>
+__global__ __launch_bounds__(256) void reduce_kernel(PddpArgs a) {
+  constexpr int MB = moment_doubles(D);
+  constexpr int NSL = (MB + 255) / 256;
+  const PLevel L = a.levels[a.level];
+  const int u = blockIdx.x / NSL, e = (blockIdx.x - u * NSL) * 256 + threadIdx.x;
+  const int bh = blockIdx.y;
+  if (e >= MB) return;
+  const PUnit U = a.units[L.unit0 + u];
+  const double *src = a.part + ((int64_t)bh * a.max_mchunks + U.chunk0) * MB + e;
+  double s = 0.0;
+  int k = 0;
+  for (; k + 8 <= U.nchunks; k += 8) {
+    double v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = src[(int64_t)(k + i) * MB];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i];
+  }
+  for (; k < U.nchunks; ++k) s += src[(int64_t)k * MB];
+  a.ured[((int64_t)bh * a.max_runits + u) * MB + e] = s;
 }
 
 // ---- node direction: grid (nnodes, BH), 256 threads -------------------------
@@ -293,11 +379,13 @@ __device__ __forceinline__ void wave_argmax(double &v, int &j) {
 
 template <int D>
 __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
-  constexpr int EPT = D * D / 256;  // covariance entries per thread
+  constexpr int NB = D / 16;
+  constexpr int NT = NB * (NB + 1) / 2;
+  constexpr int MB = moment_doubles(D);
   constexpr int PARTS = 256 / D;    // threads per column in the matrix-vector product
   constexpr int JPP = D / PARTS;    // rows per part
   __shared__ double C[D * D];
-  __shared__ double u[D], wpart[PARTS][D], red[4];
+  __shared__ double u[D], wpart[PARTS][D], red[4], mvec[D];
   __shared__ int jstar;
   const PLevel L = a.levels[a.level];
   const int bh = blockIdx.y;
@@ -305,52 +393,68 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
   const PNode nd = a.nodes[L.node0 + ln];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // covariance: add the chunk partials (upper tiles) in chunk order, every
-  // entry of this thread accumulating at once so its loads overlap. The
-  // loads are unconditional (a partial's lower tiles are in the buffer but
-  // never written) and the lower-tile values are dropped by a select, so no
-  // branch serialises them.
+  // the node's moments: its unit's (partials added in chunk order, or the
+  // reduce pass's sum), minus from the parent's for a right child; entry
+  // m * 256 + tid of the moment block is this thread's, m <= NT (m == NT: s)
   {
-    const double *cp = a.cov_part + ((int64_t)bh * a.max_chunks + nd.chunk0) * D * D;
-    double acc[EPT];
+    double val[NT + 1];
+    const bool has_s = tid < D;
+    if (L.reduced) {
+      const double *src = a.ured + ((int64_t)bh * a.max_runits + nd.unit) * MB + tid;
 #pragma unroll
-    for (int m = 0; m < EPT; ++m) acc[m] = 0.0;
-    for (int k = 0; k < nd.nchunks; ++k) {
-      const double *src = cp + (int64_t)k * D * D;
-      double v[EPT];
+      for (int m = 0; m < NT; ++m) val[m] = src[m * 256];
+      val[NT] = has_s ? src[NT * 256] : 0.0;
+    } else {
+      const PUnit U = a.units[L.unit0 + nd.unit];
+      const double *src = a.part + ((int64_t)bh * a.max_mchunks + U.chunk0) * MB + tid;
 #pragma unroll
-      for (int m = 0; m < EPT; ++m) v[m] = src[tid + 256 * m];
+      for (int m = 0; m <= NT; ++m) val[m] = 0.0;
+      for (int k = 0; k < U.nchunks; ++k) {
+        const double *p = src + (int64_t)k * MB;
+        double v[NT + 1];
 #pragma unroll
-      for (int m = 0; m < EPT; ++m) {
-        const int e = tid + 256 * m;
-        acc[m] += (((e / D) >> 4) <= ((e % D) >> 4)) ? v[m] : 0.0;
+        for (int m = 0; m < NT; ++m) v[m] = p[m * 256];
+        v[NT] = has_s ? p[NT * 256] : 0.0;
+#pragma unroll
+        for (int m = 0; m <= NT; ++m) val[m] += v[m];
       }
     }
+    if (nd.derived) {
+      const double *par = a.nodem + (((int64_t)(a.level & 1) * a.B * a.H + bh) * a.max_units + nd.unit) * MB + tid;
+      double v[NT + 1];
 #pragma unroll
-    for (int m = 0; m < EPT; ++m) {
-      const int e = tid + 256 * m;
-      if (((e / D) >> 4) <= ((e % D) >> 4)) C[e] = acc[m] / (double)nd.n;
+      for (int m = 0; m < NT; ++m) v[m] = par[m * 256];
+      v[NT] = has_s ? par[NT * 256] : 0.0;
+#pragma unroll
+      for (int m = 0; m <= NT; ++m) val[m] = v[m] - val[m];
     }
-  }
-  __syncthreads();
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, j = e - (e / D) * D;
-    if ((i >> 4) > (j >> 4)) C[e] = C[j * D + i];
-  }
-  // mean of the node for the projection kernel, partials in chunk order
-  if (tid < D) {
-    const double *mp = a.mean_part + ((int64_t)bh * a.max_chunks + nd.chunk0) * D + tid;
-    double s = 0.0;
-    int k = 0;
-    for (; k + 8 <= nd.nchunks; k += 8) {
-      double v[8];
+    if (nd.kid_unit >= 0) {
+      double *dst = a.nodem + (((int64_t)((a.level + 1) & 1) * a.B * a.H + bh) * a.max_units + nd.kid_unit) * MB + tid;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = mp[(int64_t)(k + i) * D];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s += v[i];
+      for (int m = 0; m < NT; ++m) dst[m * 256] = val[m];
+      if (has_s) dst[NT * 256] = val[NT];
     }
-    for (; k < nd.nchunks; ++k) s += mp[(int64_t)k * D];
-    a.mu[((int64_t)bh * a.max_nodes + ln) * D + tid] = s / (double)nd.n;
+    const double inv_n = 1.0 / (double)nd.n;
+    if (has_s) mvec[tid] = val[NT] * inv_n;
+    __syncthreads();
+    // covariance S/n - m m^T; the lower tiles mirror the upper ones
+    const int r = tid >> 4, c = tid & 15;
+    int m = 0;
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) {
+#pragma unroll
+      for (int bj = bi; bj < NB; ++bj, ++m) {
+        const int gi = 16 * bi + r, gj = 16 * bj + c;
+        const double x = val[m] * inv_n - mvec[gi] * mvec[gj];
+        C[gi * D + gj] = x;
+        if (bi != bj) C[gj * D + gi] = x;
+      }
+    }
+    // the node's mean for the projection kernel: c + m
+    if (has_s) {
+      const uint16_t *qh = head_q(a, bh);
+      a.mu[((int64_t)bh * a.max_nodes + ln) * D + tid] = (double)bf16_to_f32(qh[tid]) + mvec[tid];
+    }
   }
   __syncthreads();
   // start vector: e_j for the largest diagonal entry (lowest j on ties)
@@ -435,13 +539,13 @@ __global__ __launch_bounds__(256) void project_kernel(PddpArgs a) {
   constexpr int TPW = 64 / LPT;    // tokens per wave step
   const PLevel L = a.levels[a.level];
   const int bh = blockIdx.y;
-  const PChunk c = a.chunks[L.chunk0 + blockIdx.x];
+  const PChunk c = a.pchunks[L.pchunk0 + blockIdx.x];
   const uint16_t *qh = head_q(a, bh);
   const int32_t *cur = a.perm + (int64_t)bh * a.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane % LPT, tw = lane / LPT;
-  const double *mu = a.mu + ((int64_t)bh * a.max_nodes + c.node) * D + sub * 8;
-  const double *dv = a.dir + ((int64_t)bh * a.max_nodes + c.node) * D + sub * 8;
+  const double *mu = a.mu + ((int64_t)bh * a.max_nodes + c.owner) * D + sub * 8;
+  const double *dv = a.dir + ((int64_t)bh * a.max_nodes + c.owner) * D + sub * 8;
   double m8[8], u8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -549,16 +653,19 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(PddpArgs a) {
 template <int D>
 hipError_t run_levels(PddpArgs &a, const PlanCounts &pc, const std::vector<PLevel> &host_levels,
                       hipStream_t s) {
+  constexpr int NSL = (moment_doubles(D) + 255) / 256;
   const int BH = a.B * a.H;
   for (int l = 0; l < pc.levels; ++l) {
     a.level = l;
     const PLevel &L = host_levels[l];
-    const dim3 gc(L.nchunks, BH), gn(L.nnodes, BH);
-    hipLaunchKernelGGL(mean_kernel<D>, gc, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(cov_kernel<D>, gc, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(power_kernel<D>, gn, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(project_kernel<D>, gc, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(split_kernel, gn, dim3(kSplitThreads), 0, s, a);
+    if (l == 0)  // one more block builds the plan tables
+      hipLaunchKernelGGL((moment_kernel<D, true>), dim3(L.nmchunks + 1, BH), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((moment_kernel<D, false>), dim3(L.nmchunks, BH), dim3(256), 0, s, a);
+    if (L.reduced) hipLaunchKernelGGL(reduce_kernel<D>, dim3(L.nunits * NSL, BH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(power_kernel<D>, dim3(L.nnodes, BH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(project_kernel<D>, dim3(L.npchunks, BH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(split_kernel, dim3(L.nnodes, BH), dim3(kSplitThreads), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -568,7 +675,7 @@ hipError_t run_levels(PddpArgs &a, const PlanCounts &pc, const std::vector<PLeve
 }  // namespace
 
 size_t pddp_workspace_bytes(int B, int H, int N, int D, int T) {
-  const PlanCounts pc = host_plan(N, T);
+  const PlanCounts pc = host_plan(N, T, nullptr);
   return ws_layout(pc, B * H, N, D).total;
 }
 
@@ -577,16 +684,15 @@ hipError_t run_pddp(const uint16_t *q, int64_t sb, int64_t sn, int64_t sh, int B
                     hipStream_t s) {
   const int BH = B * H;
   const int64_t total = (int64_t)BH * N;
-  const int G = (N + T - 1) / T;
-  std::vector<PNode> hn(2 * G + 2);
   std::vector<PLevel> hl(kMaxLevels);
-  const PlanCounts pc = plan_tree(N, T, hl.data(), hn.data(), nullptr);
+  const PlanCounts pc = host_plan(N, T, hl.data());
   const WsLayout wl = ws_layout(pc, BH, N, D);
-  if (ws_bytes < wl.total || pc.levels > kMaxLevels) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(init_perm_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, perm,
-                     N, total);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || N <= T) return e;
+  if (ws_bytes < wl.total || pc.levels > kMaxLevels || (D != 64 && D != 128)) return hipErrorInvalidValue;
+  if (N <= T) {  // one group per head: the identity
+    hipLaunchKernelGGL(init_perm_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, perm,
+                       N, total);
+    return hipGetLastError();
+  }
   char *base = (char *)ws;
   PddpArgs a{};
   a.q = q;
@@ -596,26 +702,27 @@ hipError_t run_pddp(const uint16_t *q, int64_t sb, int64_t sn, int64_t sh, int B
   a.B = B;
   a.H = H;
   a.N = N;
+  a.T = T;
   a.perm = perm;
-  a.levels = (const PLevel *)(base + wl.levels);
-  a.nodes = (const PNode *)(base + wl.nodes);
-  a.chunks = (const PChunk *)(base + wl.chunks);
-  a.mean_part = (double *)(base + wl.mean_part);
-  a.cov_part = (double *)(base + wl.cov_part);
+  a.levels = (PLevel *)(base + wl.levels);
+  a.nodes = (PNode *)(base + wl.nodes);
+  a.units = (PUnit *)(base + wl.units);
+  a.mchunks = (PChunk *)(base + wl.mchunks);
+  a.pchunks = (PChunk *)(base + wl.pchunks);
+  a.part = (double *)(base + wl.part);
+  a.ured = (double *)(base + wl.ured);
+  a.nodem = (double *)(base + wl.nodem);
   a.mu = (double *)(base + wl.mu);
   a.dir = (double *)(base + wl.dir);
   a.proj = (double *)(base + wl.proj);
   a.tmp = (int32_t *)(base + wl.tmp);
-  a.max_chunks = pc.max_chunks;
+  a.max_mchunks = pc.max_mchunks;
+  a.max_runits = pc.max_runits > 0 ? pc.max_runits : 1;
+  a.max_units = pc.max_units;
   a.max_nodes = pc.max_nodes;
   a.power_iters = power_iters;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, s, N, T, (PLevel *)(base + wl.levels),
-                     (PNode *)(base + wl.nodes), (PChunk *)(base + wl.chunks));
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if (D == 128) return run_levels<128>(a, pc, hl, s);
-  if (D == 64) return run_levels<64>(a, pc, hl, s);
-  return hipErrorInvalidValue;
+  return run_levels<64>(a, pc, hl, s);
 }
 
 }  // namespace mcs
