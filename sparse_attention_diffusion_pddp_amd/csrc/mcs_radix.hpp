@@ -10,11 +10,13 @@ namespace mcs {
 // the candidates per 8-bit digit. Visiting digits in ascending order
 // (DESC = false) or descending order (DESC = true), it finds the first digit
 // at which the running count reaches `remaining` (1 <= remaining <= total),
-// and the lane holding it writes that digit and the count of the
-// candidates visited before it. Same answer as a sequential scan.
+// and the lane holding it writes that digit (plus digit_base) and the count
+// of the candidates visited before it (plus before_base). Same answer as a
+// sequential scan.
 template <bool DESC>
 __device__ __forceinline__ void radix_pick(const uint32_t *hist, uint32_t remaining, uint32_t *digit_out,
-                                           uint32_t *before_out) {
+                                           uint32_t *before_out, uint32_t digit_base = 0,
+                                           uint32_t before_base = 0) {
   const int lane = threadIdx.x & 63;
   uint32_t c[4];
 #pragma unroll
@@ -43,8 +45,8 @@ __device__ __forceinline__ void radix_pick(const uint32_t *hist, uint32_t remain
   const uint64_t b = __ballot(found >= 0);
   if (b != 0 && lane == __ffsll((unsigned long long)b) - 1) {
     const int r = 4 * lane + found;
-    *digit_out = (uint32_t)(DESC ? 255 - r : r);
-    *before_out = before;
+    *digit_out = digit_base + (uint32_t)(DESC ? 255 - r : r);
+    *before_out = before_base + before;
   }
 }
 

@@ -12,10 +12,12 @@
 // cross-half add; the 4 (or 2) waves' partial sums meet in LDS and are added
 // in a fixed order (no atomics).
 //
-// topk_kernel: one workgroup per (b, h, g). Radix select (4 passes of 8 bits,
-// most significant first) finds the K-th largest mass; a single ordered pass
-// with ballot prefix counts then keeps every key above it and the
-// lowest-index keys equal to it, writing their indices in ascending order.
+// topk_kernel: one workgroup per (b, h, g). A radix select, most significant
+// digit first, finds the K-th largest mass: the first digit from the whole
+// row, the rest from the first digit's bin compacted into LDS; a single
+// ordered pass with ballot prefix counts then keeps every key above it and
+// the lowest-index keys equal to it, writing their indices in ascending
+// order. Two reads of the row in all.
 #include <type_traits>
 
 #include "mcs_common.hpp"
@@ -158,39 +160,129 @@ __global__ __launch_bounds__(64 * NW, 4) void mass_kernel(SelectArgs a) {
 // top-K
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 512;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kCandCap = 15360;  // keys of the first digit's bin kept in LDS (two workgroups per CU)
+constexpr int kHCopies = 8;      // private histogram copies (lane % 8)
+constexpr int kILP = 8;          // keys loaded per thread before they are used
 
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);  // -0 and +0 are equal masses
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wave_cnt[2][kTopkThreads / 64];
-  __shared__ uint32_t sel_digit, sel_above;
+// radix_pick over 512 descending bins (one wave): the upper 256 bins first.
+__device__ __forceinline__ void pick512_desc(const uint32_t *hist, uint32_t remaining, uint32_t *digit_out,
+                                             uint32_t *before_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t up = hist[256 + 4 * lane] + hist[257 + 4 * lane] + hist[258 + 4 * lane] + hist[259 + 4 * lane];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) up += __shfl_xor(up, off);
+  if (remaining <= up) radix_pick<true>(hist + 256, remaining, digit_out, before_out, 256u, 0u);
+  else radix_pick<true>(hist, remaining - up, digit_out, before_out, 0u, up);
+}
 
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int row = work;  // (bh, g) flattened
+// One workgroup per (b, h, g) row of A. Keys are the masses' order-preserving
+// 32-bit images. The K-th largest key is found digit by digit, most
+// significant first: bits 31..23 over the whole row; then, when the chosen
+// bin's keys fit, they are compacted into LDS and bits 22..15, 14..7 and 6..0
+// are resolved there (otherwise from the row again). A last ordered pass keeps
+// every key above it and the lowest-index keys equal to it, writing their
+// indices in ascending order. Histograms are kept in kHCopies copies, picked
+// by lane % 8 at a bank-shifting stride, so equal digits within a wave
+// contend at most 8-way; the copies are added in a fixed order.
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
+  __shared__ uint32_t hc[kHCopies * 513];
+  __shared__ uint32_t hist[512];
+  __shared__ uint32_t cand[kCandCap];
+  __shared__ uint32_t eq_cnt[kTopkWaves], sel_cnt[kTopkWaves];
+  __shared__ uint32_t sel_digit, sel_above, ncand;
+
+  const int row = xcd_remap(blockIdx.x, gridDim.x);  // (bh, g) flattened
   const float *A = a.mass + (int64_t)row * a.N;
   int32_t *out = a.idx + (int64_t)row * a.K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.N;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  uint32_t prefix = 0, mask = 0;
-  uint32_t remaining = (uint32_t)a.K;  // how many of the largest are still to be placed
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
-    __syncthreads();
-    for (int j = tid; j < N; j += kTopkThreads) {
-      const uint32_t u = order_key(A[j]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+  auto clear = [&](int nb) {
+    for (int i = tid; i < kHCopies * (nb + 1); i += kTopkThreads) hc[i] = 0;
+  };
+  auto merge = [&](int nb) {
+    for (int b = tid; b < nb; b += kTopkThreads) {
+      uint32_t s = 0;
+#pragma unroll
+      for (int c = 0; c < kHCopies; ++c) s += hc[c * (nb + 1) + b];
+      hist[b] = s;
     }
+  };
+  // the row's keys, kILP per thread in flight: f(j, key) for j < N
+  auto scan_row = [&](auto f) {
+    for (int base = 0; base < N; base += kTopkThreads * kILP) {
+      uint32_t u[kILP];
+#pragma unroll
+      for (int k = 0; k < kILP; ++k) {
+        const int j = base + k * kTopkThreads + tid;
+        u[k] = order_key(A[j < N ? j : N - 1]);
+      }
+#pragma unroll
+      for (int k = 0; k < kILP; ++k) f(base + k * kTopkThreads + tid, u[k]);
+    }
+  };
+
+  // digit 1: bits 31..23 of every key
+  clear(512);
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  scan_row([&](int j, uint32_t u) {
+    if (j < N) atomicAdd(&hc[(lane & (kHCopies - 1)) * 513 + (u >> 23)], 1u);
+  });
+  __syncthreads();
+  merge(512);
+  __syncthreads();
+  if (wave == 0) pick512_desc(hist, (uint32_t)a.K, &sel_digit, &sel_above);
+  __syncthreads();
+  uint32_t prefix = sel_digit << 23, mask = 0xff800000u;
+  uint32_t remaining = (uint32_t)a.K - sel_above;  // of the largest, still to be placed
+  const bool in_lds = hist[sel_digit] <= (uint32_t)kCandCap;
+  if (in_lds) {  // compact the chosen bin's keys (any order: only values matter)
+    scan_row([&](int j, uint32_t u) {
+      const bool m = j < N && (u & mask) == prefix;
+      const uint64_t b = __ballot(m);
+      if (b != 0) {
+        uint32_t at = 0;
+        if (lane == 0) at = atomicAdd(&ncand, (uint32_t)__popcll(b));
+        at = __shfl(at, 0);
+        const uint32_t slot = at + (uint32_t)__popcll(b & lt_mask);
+        if (m && slot < (uint32_t)kCandCap) cand[slot] = u;
+      }
+    });
+    __syncthreads();
+  }
+  const int nc = in_lds ? (int)(ncand < (uint32_t)kCandCap ? ncand : (uint32_t)kCandCap) : 0;
+  // digits 2..4: bits 22..15, 14..7, 6..0
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 15 : (pass == 1 ? 7 : 0);
+    const uint32_t dm = pass == 2 ? 127u : 255u;
+    clear(256);
+    __syncthreads();
+    auto add = [&](uint32_t u) {
+      if ((u & mask) == prefix) atomicAdd(&hc[(lane & (kHCopies - 1)) * 257 + ((u >> shift) & dm)], 1u);
+    };
+    if (in_lds) {
+      for (int i = tid; i < nc; i += kTopkThreads) add(cand[i]);
+    } else {
+      scan_row([&](int j, uint32_t u) {
+        if (j < N) add(u);
+      });
+    }
+    __syncthreads();
+    merge(256);
     __syncthreads();
     if (wave == 0) radix_pick<true>(hist, remaining, &sel_digit, &sel_above);
     __syncthreads();
     prefix |= sel_digit << shift;
-    mask |= 255u << shift;
+    mask |= dm << shift;
     remaining -= sel_above;
     __syncthreads();
   }
@@ -198,43 +290,160 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   // keys equal to it, lowest index first.
   const uint32_t tau = prefix;
   const uint32_t need = remaining;
+  // Per 512-key chunk, two barriers: a wave rewrites eq_cnt only after the
+  // previous chunk's second barrier, by which every wave has read it, and
+  // sel_cnt only after this chunk's first barrier, by which every wave has
+  // read the previous chunk's.
   uint32_t written = 0, ties = 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < N; base += kTopkThreads) {
-    const int j = base + tid;
-    uint32_t u = 0;
-    if (j < N) u = order_key(A[j]);
-    const bool gt = j < N && u > tau;
-    const bool eq = j < N && u == tau;
+  scan_row([&](int j, uint32_t u) {
+    const bool ok = j < N;
+    const bool gt = ok && u > tau;
+    const bool eq = ok && u == tau;
     const uint64_t beq = __ballot(eq);
-    const uint64_t bgt = __ballot(gt);
-    if (lane == 0) {
-      wave_cnt[0][wave] = (uint32_t)__popcll(beq);
-      wave_cnt[1][wave] = (uint32_t)__popcll(bgt);
-    }
+    if (lane == 0) eq_cnt[wave] = (uint32_t)__popcll(beq);
     __syncthreads();
     uint32_t eq_before = 0, eq_total = 0;
-    for (int w = 0; w < kTopkThreads / 64; ++w) {
-      const uint32_t ce = wave_cnt[0][w];
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) {
+      const uint32_t ce = eq_cnt[w];
       eq_before += (w < wave) ? ce : 0u;
       eq_total += ce;
     }
     const uint32_t tie_rank = ties + eq_before + (uint32_t)__popcll(beq & lt_mask);
     const bool sel = gt || (eq && tie_rank < need);
     const uint64_t bsel = __ballot(sel);
-    __syncthreads();
-    if (lane == 0) wave_cnt[0][wave] = (uint32_t)__popcll(bsel);
+    if (lane == 0) sel_cnt[wave] = (uint32_t)__popcll(bsel);
     __syncthreads();
     uint32_t sel_before = 0, sel_total = 0;
-    for (int w = 0; w < kTopkThreads / 64; ++w) {
-      const uint32_t cs = wave_cnt[0][w];
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) {
+      const uint32_t cs = sel_cnt[w];
       sel_before += (w < wave) ? cs : 0u;
       sel_total += cs;
     }
-    if (sel) out[written + sel_before + (uint32_t)__popcll(bsel & lt_mask)] = j;
+    const uint32_t pos = written + sel_before + (uint32_t)__popcll(bsel & lt_mask);
+    if (sel && pos < (uint32_t)a.K) out[pos] = j;
     written += sel_total;
     ties += eq_total;
+  });
+}
+
+// Rows of up to NTH * KPT keys: the whole row is read once into registers
+// (wave w holds the contiguous segment [w * 64 * KPT, (w + 1) * 64 * KPT),
+// lane l the keys at l, l + 64, ...), every digit is resolved from the
+// registers, and each wave writes its own segment's selected indices after a
+// single barrier that gives it the counts of the segments before it.
+template <int NTH, int KPT>
+__global__ __launch_bounds__(NTH) void topk_reg_kernel(SelectArgs a) {
+  constexpr int NW = NTH / 64;
+  constexpr int SEG = 64 * KPT;
+  __shared__ uint32_t hc[kHCopies * 513];
+  __shared__ uint32_t hist[512];
+  __shared__ uint32_t gt_cnt[NW], eq_cnt[NW];
+  __shared__ uint32_t sel_digit, sel_above;
+
+  const int row = xcd_remap(blockIdx.x, gridDim.x);  // (bh, g) flattened
+  const float *A = a.mass + (int64_t)row * a.N;
+  int32_t *out = a.idx + (int64_t)row * a.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = a.N;
+  const int j0 = wave * SEG + lane;  // key k of this lane: j0 + 64 k
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t *hcl = hc + (lane & (kHCopies - 1)) * 513;
+
+  // Masses are sums of exponentials, so every key of the row has bit 31 set
+  // (a negative value, which cannot occur, would rank as +0). Slots past the
+  // row hold key 0: no digit prefix matches it and it is never above the
+  // threshold, so no per-key validity test is needed. Buffer loads: one
+  // offset register for all keys, and reads past the row return 0.
+  const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(A, (uint32_t)N * 4u);
+  const int nv = N - j0 <= 0 ? 0 : (N - j0 + 63) / 64;  // valid keys of this lane
+  uint32_t u[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const uint32_t key = order_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)j0 * 4u, 256 * k, 0)));
+    u[k] = k < nv ? (key > 0x80000000u ? key : 0x80000000u) : 0u;
+  }
+
+  // digit 1: bits 31..23
+  for (int i = tid; i < kHCopies * 513; i += NTH) hc[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) atomicAdd(&hcl[u[k] >> 23], 1u);  // key 0 lands in bin 0, never reached
+  __syncthreads();
+  for (int b = tid; b < 512; b += NTH) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int c = 0; c < kHCopies; ++c) s += hc[c * 513 + b];
+    hist[b] = s;
+  }
+  __syncthreads();
+  if (wave == 0) pick512_desc(hist, (uint32_t)a.K, &sel_digit, &sel_above);
+  __syncthreads();
+  uint32_t prefix = sel_digit << 23, mask = 0xff800000u;
+  uint32_t remaining = (uint32_t)a.K - sel_above;
+  // digits 2..4: bits 22..15, 14..7, 6..0
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 15 : (pass == 1 ? 7 : 0);
+    const uint32_t dm = pass == 2 ? 127u : 255u;
+    for (int i = tid; i < kHCopies * 257; i += NTH) hc[i] = 0;
     __syncthreads();
+    uint32_t *hcl2 = hc + (lane & (kHCopies - 1)) * 257;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      if ((u[k] & mask) == prefix) atomicAdd(&hcl2[(u[k] >> shift) & dm], 1u);
+    __syncthreads();
+    for (int b = tid; b < 256; b += NTH) {
+      uint32_t s = 0;
+#pragma unroll
+      for (int c = 0; c < kHCopies; ++c) s += hc[c * 257 + b];
+      hist[b] = s;
+    }
+    __syncthreads();
+    if (wave == 0) radix_pick<true>(hist, remaining, &sel_digit, &sel_above);
+    __syncthreads();
+    prefix |= sel_digit << shift;
+    mask |= dm << shift;
+    remaining -= sel_above;
+  }
+  const uint32_t tau = prefix;
+  const uint32_t need = remaining;
+  // the segments' counts above and equal to tau
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    gt += u[k] > tau ? 1u : 0u;
+    eq += u[k] == tau ? 1u : 0u;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    gt += __shfl_xor(gt, off);
+    eq += __shfl_xor(eq, off);
+  }
+  if (lane == 0) {
+    gt_cnt[wave] = gt;
+    eq_cnt[wave] = eq;
+  }
+  __syncthreads();
+  uint32_t written = 0, ties = 0;  // before this wave's segment
+  for (int w = 0; w < wave; ++w) {
+    const uint32_t e = eq_cnt[w];
+    const uint32_t room = need > ties ? need - ties : 0u;
+    written += gt_cnt[w] + (e < room ? e : room);
+    ties += e;
+  }
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const bool g = u[k] > tau;
+    const bool e = u[k] == tau;
+    const uint64_t beq = __ballot(e);
+    const bool sel = g || (e && ties + (uint32_t)__popcll(beq & lt_mask) < need);
+    const uint64_t bsel = __ballot(sel);
+    const uint32_t pos = written + (uint32_t)__popcll(bsel & lt_mask);
+    if (sel && pos < (uint32_t)a.K) out[pos] = j0 + 64 * k;
+    written += (uint32_t)__popcll(bsel);
+    ties += (uint32_t)__popcll(beq);
   }
 }
 
@@ -255,7 +464,13 @@ hipError_t launch_select(int head_dim, const SelectArgs &a, hipStream_t s) {
   else if (head_dim == 64 && a.T == 64) e = launch_mass<64, 2>(a, s);
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel, dim3(nblocks), dim3(kTopkThreads), 0, s, a);
+  const dim3 grid(nblocks);
+  if (a.N <= 512 * 8) hipLaunchKernelGGL((topk_reg_kernel<512, 8>), grid, dim3(512), 0, s, a);
+  else if (a.N <= 512 * 16) hipLaunchKernelGGL((topk_reg_kernel<512, 16>), grid, dim3(512), 0, s, a);
+  else if (a.N <= 512 * 32) hipLaunchKernelGGL((topk_reg_kernel<512, 32>), grid, dim3(512), 0, s, a);
+  else if (a.N <= 512 * 64) hipLaunchKernelGGL((topk_reg_kernel<512, 64>), grid, dim3(512), 0, s, a);
+  else if (a.N <= 512 * 128) hipLaunchKernelGGL((topk_reg_kernel<512, 128>), grid, dim3(512), 0, s, a);
+  else hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, s, a);
   return hipGetLastError();
 }
 
