@@ -49,7 +49,7 @@ namespace {
 
 constexpr int kChunk0 = 512;     // tokens per moment chunk at level 0
 constexpr int kChunk = 256;      // tokens per moment chunk below level 0
-constexpr int kPChunk = 1024;    // tokens per projection chunk
+constexpr int kPChunk = 256;     // tokens per projection chunk
 constexpr int kDirectChunks = 4; // a unit of at most this many chunks is summed by the power kernel
 constexpr int kMaxLevels = 40;
 constexpr int kSplitThreads = 512;
@@ -60,6 +60,7 @@ struct PLevel {
   int mchunk0, nmchunks; // moment chunks (over units)
   int pchunk0, npchunks; // projection chunks (over nodes)
   int reduced;           // 1: a reduce pass adds the units' partials
+  int maxn;              // largest node of the level (tokens)
 };
 struct PNode {
   int off, n, nl;
@@ -106,9 +107,10 @@ __host__ __device__ PlanCounts plan_tree(int N, int T, PLevel *lv, PNode *nd, PU
       most = most > x.nchunks ? most : x.nchunks;
       un[u] = x;
     }
-    int np = 0, nle = le, nue = ue;
+    int np = 0, nle = le, nue = ue, maxn = 0;
     for (int i = lb; i < le; ++i) {
       PNode x = nd[i];
+      maxn = maxn > x.n ? maxn : x.n;
       const int G = (x.n + T - 1) / T;
       x.nl = (G / 2) * T;
       const int nr = x.n - x.nl;  // nr >= nl: the right child is the larger
@@ -129,7 +131,7 @@ __host__ __device__ PlanCounts plan_tree(int N, int T, PLevel *lv, PNode *nd, PU
       nd[i] = x;
     }
     const int red = most > kDirectChunks ? 1 : 0;
-    if (lv) lv[k.levels] = PLevel{lb, le - lb, ub, ue - ub, k.mchunks, nm, k.pchunks, np, red};
+    if (lv) lv[k.levels] = PLevel{lb, le - lb, ub, ue - ub, k.mchunks, nm, k.pchunks, np, red, maxn};
     const int nn = le - lb, nu = ue - ub;
     k.max_nodes = k.max_nodes > nn ? k.max_nodes : nn;
     k.max_units = k.max_units > nu ? k.max_units : nu;
@@ -650,6 +652,123 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(PddpArgs a) {
   }
 }
 
+// ---- split of nodes up to 512 * KPT tokens: grid (nnodes, BH), 512 threads --
+// The node's keys are read once into registers (wave w holds the contiguous
+// positions [w * 64 * KPT, (w + 1) * 64 * KPT), lane l the positions l,
+// l + 64, ...); the radix passes count them into kSplitCopies private
+// histograms (lane % 8, bank-shifting stride), so equal digits within a wave
+// contend at most 8-way; and each wave partitions its own positions after a
+// single barrier that gives it the counts of the positions before it.
+constexpr int kSplitCopies = 8;
+
+template <int KPT>
+__global__ __launch_bounds__(kSplitThreads) void split_reg_kernel(PddpArgs a) {
+  constexpr int NW = kSplitThreads / 64;
+  constexpr int SEG = 64 * KPT;
+  __shared__ uint32_t hc[kSplitCopies * 257];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t lt_cnt[NW], eq_cnt[NW];
+  __shared__ uint32_t sel_digit, sel_below;
+  const PLevel L = a.levels[a.level];
+  const int bh = blockIdx.y;
+  const PNode nd = a.nodes[L.node0 + blockIdx.x];
+  const double *p = a.proj + (int64_t)bh * a.N + nd.off;
+  const int32_t *src = a.tmp + (int64_t)bh * a.N + nd.off;
+  int32_t *dst = a.perm + (int64_t)bh * a.N + nd.off;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i0 = wave * SEG + lane;  // position of key k: i0 + 64 k
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t *hcl = hc + (lane & (kSplitCopies - 1)) * 257;
+
+  // positions past the node hold the largest key: never below the
+  // threshold, which is a key of the node (the nl-th smallest, nl < n)
+  uint64_t key[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int i = i0 + 64 * k;
+    key[k] = i < nd.n ? order_key64(p[i]) : ~0ull;
+  }
+  uint64_t prefix = 0, mask = 0;
+  uint32_t remaining = (uint32_t)nd.nl;  // smallest keys still to place left
+#pragma unroll 1
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    for (int i = tid; i < kSplitCopies * 257; i += kSplitThreads) hc[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      if ((key[k] & mask) == prefix) atomicAdd(&hcl[(uint32_t)(key[k] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int cc = 0; cc < kSplitCopies; ++cc) c += hc[cc * 257 + tid];
+      hist[tid] = c;
+    }
+    __syncthreads();
+    if (wave == 0) radix_pick<false>(hist, remaining, &sel_digit, &sel_below);
+    __syncthreads();
+    prefix |= (uint64_t)sel_digit << shift;
+    mask |= (uint64_t)255 << shift;
+    remaining -= sel_below;
+  }
+  const uint64_t tau = prefix;
+  const uint32_t need = remaining;
+  uint32_t lt = 0, eq = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    lt += key[k] < tau ? 1u : 0u;
+    eq += key[k] == tau ? 1u : 0u;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lt += __shfl_xor(lt, off);
+    eq += __shfl_xor(eq, off);
+  }
+  if (lane == 0) {
+    lt_cnt[wave] = lt;
+    eq_cnt[wave] = eq;
+  }
+  __syncthreads();
+  uint32_t nleft = 0, ties = 0;  // before this wave's positions
+  for (int w = 0; w < wave; ++w) {
+    const uint32_t e = eq_cnt[w];
+    const uint32_t room = need > ties ? need - ties : 0u;
+    nleft += lt_cnt[w] + (e < room ? e : room);
+    ties += e;
+  }
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int i = i0 + 64 * k;
+    const bool e = key[k] == tau;
+    const uint64_t beq = __ballot(e);
+    const bool left = key[k] < tau || (e && ties + (uint32_t)__popcll(beq & lt_mask) < need);
+    const uint64_t bl = __ballot(left);
+    const uint32_t lrank = nleft + (uint32_t)__popcll(bl & lt_mask);
+    if (i < nd.n) {
+      const int tok = src[i];
+      if (left) dst[lrank] = tok;
+      else dst[nd.nl + (i - (int)lrank)] = tok;
+    }
+    nleft += (uint32_t)__popcll(bl);
+    ties += (uint32_t)__popcll(beq);
+  }
+}
+
+// the split of one level: register keys when its largest node fits
+hipError_t launch_split(const PddpArgs &a, const PLevel &L, int BH, hipStream_t s) {
+  const dim3 g(L.nnodes, BH), b(kSplitThreads);
+  if (L.maxn <= 512) hipLaunchKernelGGL(split_reg_kernel<1>, g, b, 0, s, a);
+  else if (L.maxn <= 512 * 2) hipLaunchKernelGGL(split_reg_kernel<2>, g, b, 0, s, a);
+  else if (L.maxn <= 512 * 4) hipLaunchKernelGGL(split_reg_kernel<4>, g, b, 0, s, a);
+  else if (L.maxn <= 512 * 8) hipLaunchKernelGGL(split_reg_kernel<8>, g, b, 0, s, a);
+  else if (L.maxn <= 512 * 16) hipLaunchKernelGGL(split_reg_kernel<16>, g, b, 0, s, a);
+  else if (L.maxn <= 512 * 32) hipLaunchKernelGGL(split_reg_kernel<32>, g, b, 0, s, a);
+  else if (L.maxn <= 512 * 64) hipLaunchKernelGGL(split_reg_kernel<64>, g, b, 0, s, a);
+  else hipLaunchKernelGGL(split_kernel, g, b, 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t run_levels(PddpArgs &a, const PlanCounts &pc, const std::vector<PLevel> &host_levels,
                       hipStream_t s) {
@@ -665,8 +784,7 @@ hipError_t run_levels(PddpArgs &a, const PlanCounts &pc, const std::vector<PLeve
     if (L.reduced) hipLaunchKernelGGL(reduce_kernel<D>, dim3(L.nunits * NSL, BH), dim3(256), 0, s, a);
     hipLaunchKernelGGL(power_kernel<D>, dim3(L.nnodes, BH), dim3(256), 0, s, a);
     hipLaunchKernelGGL(project_kernel<D>, dim3(L.npchunks, BH), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(split_kernel, dim3(L.nnodes, BH), dim3(kSplitThreads), 0, s, a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_split(a, L, BH, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
