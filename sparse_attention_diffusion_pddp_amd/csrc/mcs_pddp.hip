@@ -386,8 +386,9 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
   constexpr int MB = moment_doubles(D);
   constexpr int PARTS = 256 / D;    // threads per column in the matrix-vector product
   constexpr int JPP = D / PARTS;    // rows per part
-  __shared__ double C[D * D];
-  __shared__ double u[D], wpart[PARTS][D], red[4], mvec[D];
+  constexpr int CS = 33;            // row stride (doubles) of the 32-column exchange buffer
+  __shared__ double Cb[D * CS];
+  __shared__ double u[D], wpart[PARTS][D], red[4], mvec[D], diag[D];
   __shared__ int jstar;
   const PLevel L = a.levels[a.level];
   const int bh = blockIdx.y;
@@ -395,6 +396,7 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
   const PNode nd = a.nodes[L.node0 + ln];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  double creg[JPP];  // this thread's rows of one column of C (filled below)
   // the node's moments: its unit's (partials added in chunk order, or the
   // reduce pass's sum), minus from the parent's for a right child; entry
   // m * 256 + tid of the moment block is this thread's, m <= NT (m == NT: s)
@@ -439,7 +441,7 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
     const double inv_n = 1.0 / (double)nd.n;
     if (has_s) mvec[tid] = val[NT] * inv_n;
     __syncthreads();
-    // covariance S/n - m m^T; the lower tiles mirror the upper ones
+    // covariance S/n - m m^T, upper tiles, in place
     const int r = tid >> 4, c = tid & 15;
     int m = 0;
 #pragma unroll
@@ -447,9 +449,8 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
 #pragma unroll
       for (int bj = bi; bj < NB; ++bj, ++m) {
         const int gi = 16 * bi + r, gj = 16 * bj + c;
-        const double x = val[m] * inv_n - mvec[gi] * mvec[gj];
-        C[gi * D + gj] = x;
-        if (bi != bj) C[gj * D + gi] = x;
+        val[m] = val[m] * inv_n - mvec[gi] * mvec[gj];
+        if (bi == bj && r == c) diag[gi] = val[m];
       }
     }
     // the node's mean for the projection kernel: c + m
@@ -457,31 +458,49 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
       const uint16_t *qh = head_q(a, bh);
       a.mu[((int64_t)bh * a.max_nodes + ln) * D + tid] = (double)bf16_to_f32(qh[tid]) + mvec[tid];
     }
-  }
-  __syncthreads();
-  // start vector: e_j for the largest diagonal entry (lowest j on ties)
-  if (wave == 0) {
-    double v = C[lane * D + lane];
-    int j = lane;
-    if (D > 64) {
-      const double v2 = C[(lane + 64) * D + lane + 64];
-      if (v2 > v) {
-        v = v2;
-        j = lane + 64;
+    __syncthreads();
+    // start vector: e_j for the largest diagonal entry (lowest j on ties)
+    if (wave == 0) {
+      double v = diag[lane];
+      int j = lane;
+      if (D > 64) {
+        const double v2 = diag[lane + 64];
+        if (v2 > v) {
+          v = v2;
+          j = lane + 64;
+        }
       }
+      wave_argmax(v, j);
+      if (lane == 0) jstar = j;
     }
-    wave_argmax(v, j);
-    if (lane == 0) jstar = j;
+    // thread (part, col) keeps rows part, part + PARTS, ... of column col of
+    // C in registers for all iterations (C is symmetric: column = row). C
+    // reaches them 32 columns at a time through Cb: the upper tiles as they
+    // are, the lower ones mirrored, so a block needs 33 KB of LDS, not
+    // 128 KB, and two blocks share a CU.
+#pragma unroll
+    for (int pc = 0; pc < D / 32; ++pc) {
+      int mt = 0;
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) {
+#pragma unroll
+        for (int bj = bi; bj < NB; ++bj, ++mt) {
+          const int gi = 16 * bi + r, gj = 16 * bj + c;
+          if ((bj >> 1) == pc) Cb[gi * CS + (gj - 32 * pc)] = val[mt];
+          if (bi != bj && (bi >> 1) == pc) Cb[gj * CS + (gi - 32 * pc)] = val[mt];
+        }
+      }
+      __syncthreads();
+      if (((tid % D) >> 5) == pc) {
+#pragma unroll
+        for (int mm = 0; mm < JPP; ++mm) creg[mm] = Cb[(tid / D + PARTS * mm) * CS + (tid % D - 32 * pc)];
+      }
+      __syncthreads();
+    }
   }
-  __syncthreads();
   if (tid < D) u[tid] = (tid == jstar) ? 1.0 : 0.0;
   __syncthreads();
-  // thread (part, col) keeps rows part, part + PARTS, ... of column col of
-  // C in registers for all iterations (C is symmetric: column = row)
   const int col = tid % D, part = tid / D;
-  double creg[JPP];
-#pragma unroll
-  for (int m = 0; m < JPP; ++m) creg[m] = C[(part + PARTS * m) * D + col];
   for (int it = 0; it < a.power_iters; ++it) {
     // w = C u, this thread's rows; two accumulators for ILP
     double s0 = 0.0, s1 = 0.0;
