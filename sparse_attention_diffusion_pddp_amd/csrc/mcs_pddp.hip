@@ -220,7 +220,7 @@ __device__ __forceinline__ const uint16_t *head_q(const PddpArgs &a, int bh) {
 // Tokens are staged through LDS as float64 (x - c), SUB at a time, the next
 // SUB rows already loaded into registers while the MFMAs run on these.
 template <int D, bool L0>
-__global__ __launch_bounds__(256) void moment_kernel(PddpArgs a) {
+__global__ __launch_bounds__(256, 2) void moment_kernel(PddpArgs a) {
   constexpr int NB = D / 16;                 // 16-wide dim blocks
   constexpr int NT = NB * (NB + 1) / 2;      // upper-triangle tiles
   constexpr int TPW = (NT + 3) / 4;          // tiles per wave (at most)
@@ -254,19 +254,33 @@ __global__ __launch_bounds__(256) void moment_kernel(PddpArgs a) {
   const uint16_t *qh = head_q(a, bh);
   const int col = tid % CH, tl = tid / CH;
 
-  double cv[8];
+  float cv[8];  // token 0 of the head (bf16 values: exact as float)
   {
-    const u32x4 v = *(const u32x4 *)(qh + col * 8);  // token 0 of the head
+    const u32x4 v = *(const u32x4 *)(qh + col * 8);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      cv[2 * m] = (double)bf16_to_f32(v[m] & 0xffffu);
-      cv[2 * m + 1] = (double)bf16_to_f32(v[m] >> 16);
+      cv[2 * m] = bf16_to_f32(v[m] & 0xffffu);
+      cv[2 * m + 1] = bf16_to_f32(v[m] >> 16);
     }
   }
   double sx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // wave w owns the upper-triangle tiles t = 4k + w (t enumerates (bi, bj),
+  // bi <= bj, row-major); acc[k] accumulates tile 4k + w, whose operands
+  // start at columns ao[k] = 16 bi and bo[k] = 16 bj (wave-uniform, so the
+  // MFMA loop has no branches and fixed accumulators)
   f64x4 acc[TPW];
+  int ao[TPW], bo[TPW];
 #pragma unroll
-  for (int k = 0; k < TPW; ++k) acc[k] = f64x4{0, 0, 0, 0};
+  for (int k = 0; k < TPW; ++k) {
+    acc[k] = f64x4{0, 0, 0, 0};
+    int rem = 4 * k + wave, bi = 0;
+    while (bi < NB && rem >= NB - bi) {
+      rem -= NB - bi;
+      ++bi;
+    }
+    ao[k] = 16 * (bi < NB ? bi : 0);
+    bo[k] = 16 * (bi < NB ? bi + rem : 0);
+  }
 
   u32x4 pre[RPT];
   bool ok[RPT];
@@ -287,8 +301,8 @@ __global__ __launch_bounds__(256) void moment_kernel(PddpArgs a) {
       double x[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        x[2 * m] = ok[r] ? (double)bf16_to_f32(pre[r][m] & 0xffffu) - cv[2 * m] : 0.0;
-        x[2 * m + 1] = ok[r] ? (double)bf16_to_f32(pre[r][m] >> 16) - cv[2 * m + 1] : 0.0;
+        x[2 * m] = ok[r] ? (double)bf16_to_f32(pre[r][m] & 0xffffu) - (double)cv[2 * m] : 0.0;
+        x[2 * m + 1] = ok[r] ? (double)bf16_to_f32(pre[r][m] >> 16) - (double)cv[2 * m + 1] : 0.0;
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -300,18 +314,17 @@ __global__ __launch_bounds__(256) void moment_kernel(PddpArgs a) {
     if (base + SUB < len) fetch(base + SUB);
     const int steps = (len - base) < SUB ? ((len - base + 3) / 4) : SUB / 4;
     for (int s = 0; s < steps; ++s) {
-      const int row = 4 * s + (lane >> 4);
-      double fr[NB];
+      const double *xr = X + (4 * s + (lane >> 4)) * XS + (lane & 15);
+      double fa[TPW], fb[TPW];  // every operand of the step in flight at once
 #pragma unroll
-      for (int bb = 0; bb < NB; ++bb) fr[bb] = X[row * XS + 16 * bb + (lane & 15)];
-      int t = 0;
+      for (int k = 0; k < TPW; ++k) {
+        fa[k] = xr[ao[k]];
+        fb[k] = xr[bo[k]];
+      }
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi) {
-#pragma unroll
-        for (int bj = bi; bj < NB; ++bj, ++t) {
-          if ((t & 3) == wave)
-            acc[t >> 2] = __builtin_amdgcn_mfma_f64_16x16x4f64(fr[bi], fr[bj], acc[t >> 2], 0, 0, 0);
-        }
+      for (int k = 0; k < TPW; ++k) {
+        if (4 * k + 3 < NT || 4 * k + wave < NT)
+          acc[k] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[k], fb[k], acc[k], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -326,16 +339,13 @@ __global__ __launch_bounds__(256) void moment_kernel(PddpArgs a) {
     for (int t = 0; t < TL; ++t) s += X[t * XS + tid];
     out[NT * 256 + tid] = s;
   }
-  int t = 0;
 #pragma unroll
-  for (int bi = 0; bi < NB; ++bi) {
+  for (int k = 0; k < TPW; ++k) {
+    const int t = 4 * k + wave;
+    if (t < NT) {
 #pragma unroll
-    for (int bj = bi; bj < NB; ++bj, ++t) {
-      if ((t & 3) == wave) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)  // f64 MFMA: row = lane/16 + 4*i, column = lane % 16
-          out[t * 256 + ((lane >> 4) + 4 * i) * 16 + (lane & 15)] = acc[t >> 2][i];
-      }
+      for (int i = 0; i < 4; ++i)  // f64 MFMA: row = lane/16 + 4*i, column = lane % 16
+        out[t * 256 + ((lane >> 4) + 4 * i) * 16 + (lane & 15)] = acc[k][i];
     }
   }
 }
