@@ -1,0 +1,46 @@
+"""PDDP groups at the shapes the full-size tests do not reach, bit-exact
+against the oracle.
+
+The full-size tests group at d = 128, T = 128. These cover:
+* d = 64, whose moment kernel gives its last tile slot to two waves only
+  (10 upper-triangle tiles over 4 waves);
+* T = 64 trees;
+* the reduce pass (units of more than 4 moment chunks) at both widths;
+* register splits of 4-64 keys per thread at d = 64.
+
+Every head uses the clustered generator of the pages' video workloads."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_diffusion_pddp_amd import binding as mcs
+from sparse_attention_diffusion_pddp_amd import synth
+from tests import parity_util as U
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    # (N, d, T, heads)
+    (5000, 64, 64, 2),
+    (9000, 128, 64, 1),
+    (4500, 64, 128, 2),
+    (33000, 64, 128, 1),
+]
+
+
+@pytest.mark.parametrize("N,d,T,H", SHAPES)
+def test_pddp_groups_exact(lib, N, d, T, H):
+    print(f"\n[pddp N={N} d={d} T={T} H={H}]", flush=True)
+    w = synth.small_workload(N, heads=H, head_dim=d, group_size=T, density_pct=15)
+    q = synth.make_qkv(w, seed=N + d + T)[0]
+    dq = q.cuda()
+    desc = mcs.desc_for(dq)
+    ws = torch.empty(mcs.pddp_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+    perm = torch.empty((1, H, N), dtype=torch.int32, device="cuda")
+    mcs.pddp_group(dq, T, perm, ws)
+    torch.cuda.synchronize()
+    got = perm.cpu().numpy()
+    for h in range(H):
+        want = O.pddp_group(U.head_np(q, 0, h), T)
+        assert np.array_equal(got[0, h], want), f"head {h}: groups differ"
