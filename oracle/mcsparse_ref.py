@@ -37,13 +37,18 @@ Readings where the pages are silent (each is listed in the design doc):
     indices are stored ascending;
   * sparse attention = softmax renormalised over the selected keys;
   * R is rounded to bf16 (RNE) from the stored bf16 dense output; the reuse
-    output is bf16(sparse + R).
+    output is bf16(sparse + R);
+  * whitening for PDDP (listed on the news page only as an open item, never
+    defined) = per-dimension standardization of the head's queries before
+    grouping. The root's power iteration starts at the lowest dimension of
+    nonzero variance, since exact arithmetic ties every standardized variance
+    at 1.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_*.py`` (closed forms, brute force in exact decimal
 arithmetic, library routines, invariants). The only unpinned claim is that
-this reading of "Fast PDDP" reproduces the authors' groups: the pages print
-no groups to check against.
+this reading of "Fast PDDP" (and of its whitening) reproduces the authors'
+groups: the pages print no groups to check against.
 """
 from __future__ import annotations
 
@@ -56,6 +61,7 @@ __all__ = [
     "topk_count",
     "pddp_group",
     "principal_direction",
+    "standardize",
     "dense_lse",
     "group_mass",
     "topk_select",
@@ -105,17 +111,18 @@ def topk_count(density_pct: int, seqlen: int) -> int:
 # step 1: Fast PDDP query grouping
 # ---------------------------------------------------------------------------
 
-def principal_direction(C: np.ndarray, power_iters: int = 16) -> np.ndarray:
+def principal_direction(C: np.ndarray, power_iters: int = 16, start: int | None = None) -> np.ndarray:
     """Leading eigenvector of the symmetric PSD matrix C by power iteration.
 
-    u0 = e_j with j = argmax_j C_jj (lowest j on ties); then exactly
-    ``power_iters`` steps of u <- C u / ||C u||. If C u is the zero vector the
-    direction is the zero vector (every projection is then 0). The result is
-    oriented so that its largest-magnitude component is positive.
+    u0 = e_j with j = argmax_j C_jj (lowest j on ties), or j = ``start`` when
+    given; then exactly ``power_iters`` steps of u <- C u / ||C u||. If C u is
+    the zero vector the direction is the zero vector (every projection is
+    then 0). The result is oriented so that its largest-magnitude component
+    is positive.
     """
     d = C.shape[0]
     u = np.zeros(d)
-    u[int(np.argmax(np.diag(C)))] = 1.0
+    u[int(np.argmax(np.diag(C))) if start is None else int(start)] = 1.0
     for _ in range(power_iters):
         w = C @ u
         nrm = math.sqrt(float(np.dot(w, w)))
@@ -126,14 +133,14 @@ def principal_direction(C: np.ndarray, power_iters: int = 16) -> np.ndarray:
     return -u if u[j] < 0 else u
 
 
-def _split_node(q: np.ndarray, members: np.ndarray, n_left: int, power_iters: int):
+def _split_node(q: np.ndarray, members: np.ndarray, n_left: int, power_iters: int, start: int | None = None):
     """One PDDP split: centre, covariance, principal direction, projection, rank split."""
     X = q[members]
     n = X.shape[0]
     mu = X.sum(axis=0) / n
     Xc = X - mu
     C = (Xc.T @ Xc) / n
-    u = principal_direction(C, power_iters)
+    u = principal_direction(C, power_iters, start)
     p = (Xc * u[None, :]).sum(axis=1)  # row by row: identical rows give identical p
     order = np.lexsort((members, p))  # by projection, then by token index
     left = np.sort(members[order[:n_left]])
@@ -141,7 +148,26 @@ def _split_node(q: np.ndarray, members: np.ndarray, n_left: int, power_iters: in
     return left, right
 
 
-def pddp_group(q: np.ndarray, group_size: int, power_iters: int = 16) -> np.ndarray:
+def standardize(q: np.ndarray):
+    """Whitening as this oracle reads it: every dimension of the head's
+    queries centred and scaled to unit variance over the head's N tokens.
+
+    The pages list whitening for PDDP only as an open item and never define
+    it. Full whitening would make the root's covariance the identity, with
+    no principal direction to split on. So the reading is the per-dimension
+    one: x'_d = (x_d - mu_d) / sigma_d, with sigma_d the population standard
+    deviation. A dimension of zero variance is left unscaled; it is all zero
+    once centred. Returns (x', var).
+    """
+    N = q.shape[0]
+    mu = q.sum(axis=0) / N
+    Xc = q - mu
+    var = (Xc * Xc).sum(axis=0) / N
+    scale = np.where(var > 0, 1.0 / np.sqrt(np.where(var > 0, var, 1.0)), 1.0)
+    return Xc * scale, var
+
+
+def pddp_group(q: np.ndarray, group_size: int, power_iters: int = 16, whiten: bool = False) -> np.ndarray:
     """Fast PDDP grouping of one head's queries ``q [N, d]``.
 
     Returns ``perm [N]`` (int64): group g is ``perm[g*T : min((g+1)*T, N)]``,
@@ -149,11 +175,23 @@ def pddp_group(q: np.ndarray, group_size: int, power_iters: int = 16) -> np.ndar
     when G_S == 1; otherwise its first floor(G_S/2)*T tokens in (projection,
     index) order form the left child, the rest the right child, and the left
     child's groups come first.
+
+    ``whiten``: the same recursion on ``standardize(q)``. Its root covariance
+    has every nonzero variance equal to 1 in exact arithmetic, so the tie
+    rule starts the root's power iteration at the lowest dimension of
+    nonzero variance. That decision is taken exactly here, not from the
+    rounded diagonal.
     """
     N = q.shape[0]
     T = int(group_size)
+    root_start = None
+    if whiten:
+        q, var = standardize(q)
+        nz = np.nonzero(var > 0)[0]
+        root_start = int(nz[0]) if nz.size else 0
     out = []
     stack = [np.arange(N, dtype=np.int64)]
+    root = True
     while stack:
         members = stack.pop()
         n = members.shape[0]
@@ -161,7 +199,8 @@ def pddp_group(q: np.ndarray, group_size: int, power_iters: int = 16) -> np.ndar
         if G <= 1:
             out.append(np.sort(members))
             continue
-        left, right = _split_node(q, members, (G // 2) * T, power_iters)
+        left, right = _split_node(q, members, (G // 2) * T, power_iters, root_start if root else None)
+        root = False
         stack.append(right)  # popped after the whole left subtree
         stack.append(left)
     perm = np.concatenate(out) if out else np.zeros(0, dtype=np.int64)

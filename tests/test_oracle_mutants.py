@@ -47,12 +47,12 @@ def _residual_flipped(o_dense_stored, o_sparse):
     return ref.round_bf16(o_sparse - o_dense_stored)
 
 
-def _pd_15(C, power_iters=16):
-    return ref.__dict__["_orig_principal_direction"](C, 15)
+def _pd_15(C, power_iters=16, start=None):
+    return ref.__dict__["_orig_principal_direction"](C, 15, start)
 
 
-def _pd_no_orientation(C, power_iters=16):
-    u = ref.__dict__["_orig_principal_direction"](C, power_iters)
+def _pd_no_orientation(C, power_iters=16, start=None):
+    u = ref.__dict__["_orig_principal_direction"](C, power_iters, start)
     return -u
 
 
@@ -60,6 +60,25 @@ def _sparse_unnormalised(q_rows, k, v, idx, scale):
     ks, vs = k[idx], v[idx]
     s = scale * (q_rows @ ks.T)
     return np.exp(s - s.max(axis=1, keepdims=True)) @ vs
+
+
+def _std_unscaled(q):
+    Xc, var = ref.__dict__["_orig_standardize"](q)
+    return q - q.sum(axis=0) / q.shape[0], var  # centred, never scaled
+
+
+def _std_by_variance(q):
+    N = q.shape[0]
+    Xc = q - q.sum(axis=0) / N
+    var = (Xc * Xc).sum(axis=0) / N
+    return Xc / np.where(var > 0, var, 1.0), var  # 1/var instead of 1/sd
+
+
+def _std_times_sd(q):
+    N = q.shape[0]
+    Xc = q - q.sum(axis=0) / N
+    var = (Xc * Xc).sum(axis=0) / N
+    return Xc * np.sqrt(var), var  # inverted scale
 
 
 MUTANTS = [
@@ -72,6 +91,9 @@ MUTANTS = [
     ("principal_direction", _pd_15, pins.test_principal_direction_closed_form_iteration_count),
     ("principal_direction", _pd_no_orientation, pins.test_pddp_rank_one_reduces_to_argsort_chunks),
     ("sparse_attention", _sparse_unnormalised, pins.test_sparse_decimal_bruteforce),
+    ("standardize", _std_unscaled, pins.test_whitened_pddp_root_split_follows_the_correlation_eigenvector),
+    ("standardize", _std_by_variance, pins.test_whitened_pddp_root_split_follows_the_correlation_eigenvector),
+    ("standardize", _std_times_sd, pins.test_standardize_closed_form_and_constant_dims),
 ]
 
 

@@ -355,6 +355,77 @@ def test_pddp_first_split_is_median_of_projection():
     assert sorted(perm[:2 * T].tolist()) == sorted(order[:2 * T].tolist())
 
 
+def _three_factor_queries(rng, N):
+    """Three independent factors: a on dim 0 at scale 100, b on dims 1-5 at
+    scale 1, c on dims 6-7 at scale 0.01, each dim with 5% noise of its own
+    scale. Raw variance is dominated by a. After per-dimension
+    standardization the b block (five correlated dims) carries the largest
+    correlation eigenvalue (~5, against ~2 for c and ~1 for a; 16 power
+    iterations leave (2/5)^16 ~ 4e-7 of c). Scaling by 1/variance instead
+    would favour c."""
+    a, b, c = rng.standard_normal(N), rng.standard_normal(N), rng.standard_normal(N)
+    cols = [100 * a] + [b] * 5 + [0.01 * c] * 2
+    scales = [100, 1, 1, 1, 1, 1, 0.01, 0.01]
+    q = np.stack([col + 0.05 * sc * rng.standard_normal(N) for col, sc in zip(cols, scales)], axis=1)
+    return q, a, b, c
+
+
+def test_whitened_pddp_root_split_follows_the_correlation_eigenvector():
+    """Whitening (per-dimension standardization): the root split puts left the
+    tokens below the median projection on the top eigenvector of the
+    correlation matrix (numpy's eigh), the b factor here. The plain split
+    follows the covariance's top eigenvector, the a factor. The two left sets
+    differ."""
+    rng = np.random.default_rng(21)
+    N, T = 4 * 64, 64
+    q, a, b, c = _three_factor_queries(rng, N)
+    Z = (q - q.mean(axis=0)) / q.std(axis=0)
+    evals, evecs = np.linalg.eigh(np.corrcoef(q, rowvar=False))
+    assert evals[-1] > 4.5 and evals[-2] < 2.2  # a clear gap: b's block first
+    top = evecs[:, -1]
+    top = top if top[np.argmax(np.abs(top))] > 0 else -top
+    p = Z @ top
+    want = sorted(np.lexsort((np.arange(N), p))[:2 * T].tolist())
+    got = sorted(O.pddp_group(q, T, whiten=True)[:2 * T].tolist())
+    assert got == want
+    # plain PDDP splits along dim 0 (the a factor), up to the few tokens the
+    # other dims' small weight in its direction can move across the median
+    plain = set(O.pddp_group(q, T)[:2 * T].tolist())
+    low0, high0 = set(np.argsort(q[:, 0])[:2 * T].tolist()), set(np.argsort(-q[:, 0])[:2 * T].tolist())
+    assert max(len(plain & low0), len(plain & high0)) >= 2 * T - 4
+    assert len(plain & set(want)) < 1.6 * T  # a and b are independent
+
+
+def test_whitened_pddp_is_exactly_invariant_to_power_of_two_dim_scaling():
+    """Scaling one dimension by 4 (or 1/4) is exact in floating point, and
+    standardization removes it exactly, so the whitened groups are bitwise
+    the same. The plain groups are not invariant: the same scaling changes
+    them."""
+    from sparse_attention_diffusion_pddp_amd.synth import make_qkv, small_workload
+    w = small_workload(640, heads=1, head_dim=16, group_size=64, density_pct=15)
+    q = make_qkv(w, seed=22, dtype=torch.float32)[0][0, :, 0, :].double().numpy()
+    q2 = q.copy()
+    q2[:, 5] *= 4.0
+    q2[:, 2] *= 0.25
+    assert np.array_equal(O.pddp_group(q, 64, whiten=True), O.pddp_group(q2, 64, whiten=True))
+    assert not np.array_equal(O.pddp_group(q, 64), O.pddp_group(q2, 64))
+
+
+def test_standardize_closed_form_and_constant_dims():
+    q = np.array([[1.0, 5.0, 2.0], [3.0, 5.0, 2.0], [5.0, 5.0, 8.0], [7.0, 5.0, 8.0]])
+    z, var = O.standardize(q)
+    # dim 0: mean 4, variance 5; dim 1 constant: variance 0, left unscaled (all 0);
+    # dim 2: mean 5, variance 9
+    np.testing.assert_array_equal(var, [5.0, 0.0, 9.0])
+    np.testing.assert_allclose(z[:, 0], np.array([-3.0, -1.0, 1.0, 3.0]) / math.sqrt(5.0), rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(z[:, 1], 0.0)
+    np.testing.assert_array_equal(z[:, 2], [-1.0, -1.0, 1.0, 1.0])
+    # the whitened tree starts its root at the lowest dim of nonzero variance
+    # and still yields a tiled bijection
+    perm = O.pddp_group(np.repeat(q, 40, axis=0), 32, whiten=True)
+    _check_perm(perm, 160, 32)
+
+
 def test_topk_count_integer_ceil():
     assert O.topk_count(25, 1024) == 256
     assert O.topk_count(15, 32760) == 4914
