@@ -354,8 +354,9 @@ def run_kernel_only(args, w):
 
 def run_variants(args, w):
     """Selection variants on synthetic data, the ablation axes of the paper
-    landing page (Tables 3-4): query order (PDDP groups vs consecutive
-    tokens) x selection granularity (single keys vs 64-key blocks), at the
+    landing page (Tables 3-4): query order (PDDP groups, whitened PDDP
+    groups, or consecutive tokens) x selection granularity (single keys vs
+    64-key blocks), at the
     same realised density. Per variant: recall = mean over groups of the
     selected keys' share of the group's exact probability mass; the sparse
     output's relative L1 error against dense at the anchor (no R); and the
@@ -393,14 +394,24 @@ def run_variants(args, w):
 
     ws = torch.empty(mcs.pddp_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
     perm_pddp = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
-    mcs.pddp_group(q, T, perm_pddp, ws)
+    perm_white = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    grouping_ms = {}
+    for name, perm_, white in (("pddp", perm_pddp, False), ("pddp_whitened", perm_white, True)):
+        mcs.pddp_group(q, T, perm_, ws, whiten=white)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            mcs.pddp_group(q, T, perm_, ws, whiten=white)
+        e1.record()
+        torch.cuda.synchronize()
+        grouping_ms[name] = round(e0.elapsed_time(e1) / 5, 3)
     perm_none = torch.arange(N, dtype=torch.int32, device="cuda").expand(B, H, N).contiguous()
     sizes = torch.full((G,), float(T), device="cuda")
     sizes[-1] = N - (G - 1) * T
     mass = torch.empty((B, H, G, N), dtype=torch.float32, device="cuda")
     out = torch.empty_like(q)
     rows = []
-    for order, perm in (("pddp", perm_pddp), ("none", perm_none)):
+    for order, perm in (("pddp", perm_pddp), ("pddp_whitened", perm_white), ("none", perm_none)):
         idx_tok = torch.empty((B, H, G, K), dtype=torch.int32, device="cuda")
         mcs.anchor_select_topk(q, k, lse0, perm, T, K, idx_tok, group_mass=mass)
         full = (N // BLK) * BLK
@@ -425,7 +436,7 @@ def run_variants(args, w):
     print(json.dumps({"workload": w.name, "config": {"heads": H, "seqlen": N, "head_dim": d, "group_size": T,
                                                      "density_pct": w.density_pct, "reuse_steps": len(dev) - 1,
                                                      "drift": w.drift, "seed": args.seed},
-                      "variants": rows}), flush=True)
+                      "grouping_ms": grouping_ms, "variants": rows}), flush=True)
 
 
 def main():

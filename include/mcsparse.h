@@ -106,6 +106,24 @@ mcs_status_t mcs_pddp_group(const mcs_attn_desc_t *desc, const void *q, int32_t 
                             int32_t power_iters, int32_t *perm, void *ws, size_t ws_bytes,
                             mcs_stream_t stream);
 
+/* Step 1 with options. mcs_pddp_group is this call with flags = 0.
+ *   MCS_PDDP_WHITEN: whitened grouping. Whitening is listed on the news page
+ *     only as an open item of the authors, never defined; this library reads
+ *     it as per-dimension standardization. Every query dimension is centred
+ *     and scaled to unit variance over the head's N tokens (population
+ *     variance, float64), and a zero-variance dimension is left unscaled.
+ *     The recursion above then runs on the standardized queries, so each
+ *     node's covariance becomes W C W with W = diag(1/sigma). The root's
+ *     power iteration starts at the lowest dimension of nonzero variance:
+ *     exact arithmetic ties every standardized root variance at 1. The
+ *     workspace size is the same as without the flag.
+ *   Other flag bits: MCS_ERR_INVALID_ARGUMENT.
+ */
+#define MCS_PDDP_WHITEN 1u
+mcs_status_t mcs_pddp_group_ex(const mcs_attn_desc_t *desc, const void *q, int32_t group_size,
+                               int32_t power_iters, uint32_t flags, int32_t *perm, void *ws,
+                               size_t ws_bytes, mcs_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Step 2a: anchor dense attention with per-row log-sum-exp (research
  * walkthrough page, method step 2: dense attention and each row's LSE first).

@@ -29,6 +29,7 @@ SIGNATURES = [
     ("mcs_last_error", ctypes.c_char_p, []),
     ("mcs_pddp_group_workspace_size", _i32, [_p, _i32, ctypes.POINTER(_sz)]),
     ("mcs_pddp_group", _i32, [_p, _p, _i32, _i32, _p, _p, _sz, _p]),
+    ("mcs_pddp_group_ex", _i32, [_p, _p, _i32, _i32, ctypes.c_uint32, _p, _p, _sz, _p]),
     ("mcs_anchor_dense_lse", _i32, [_p, _p, _p, _p, _p, _p, _p]),
     ("mcs_anchor_select_topk_workspace_size", _i32, [_p, _i32, _i32, ctypes.POINTER(_sz)]),
     ("mcs_anchor_select_topk", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _sz, _p]),
@@ -126,9 +127,17 @@ def select_workspace_size(desc: Desc, group_size: int, topk: int) -> int:
     return n.value
 
 
-def pddp_group(q, group_size, perm, ws, power_iters=16, desc=None, stream=None):
+PDDP_WHITEN = 1  # MCS_PDDP_WHITEN
+
+
+def pddp_group(q, group_size, perm, ws, power_iters=16, desc=None, stream=None, whiten=False):
     lib = load()
     desc = desc or desc_for(q)
+    if whiten:
+        _check("mcs_pddp_group_ex", lib.mcs_pddp_group_ex(ctypes.byref(desc), _ptr(q), group_size, power_iters,
+                                                          PDDP_WHITEN, _ptr(perm), _ptr(ws),
+                                                          ws.numel() * ws.element_size(), _stream(stream)))
+        return
     _check("mcs_pddp_group", lib.mcs_pddp_group(ctypes.byref(desc), _ptr(q), group_size, power_iters, _ptr(perm),
                                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 

@@ -136,22 +136,30 @@ mcs_status_t mcs_pddp_group_workspace_size(const mcs_attn_desc_t *desc, int32_t 
   return ok();
 }
 
-mcs_status_t mcs_pddp_group(const mcs_attn_desc_t *desc, const void *q, int32_t group_size,
-                            int32_t power_iters, int32_t *perm, void *ws, size_t ws_bytes,
-                            mcs_stream_t stream) {
+mcs_status_t mcs_pddp_group_ex(const mcs_attn_desc_t *desc, const void *q, int32_t group_size,
+                               int32_t power_iters, uint32_t flags, int32_t *perm, void *ws,
+                               size_t ws_bytes, mcs_stream_t stream) {
   MCS_TRY(check_desc(desc));
   MCS_TRY(check_group(group_size));
   MCS_TRY(check_tensor(q, "q"));
   MCS_TRY(check_ptr(perm, "perm"));
   if (power_iters < 1 || power_iters > 64)
     return fail(MCS_ERR_INVALID_ARGUMENT, "power_iters %d outside [1, 64]", power_iters);
+  if (flags & ~MCS_PDDP_WHITEN) return fail(MCS_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
   const size_t need = mcs::pddp_workspace_bytes(desc->batch, desc->heads, desc->seqlen, desc->head_dim, group_size);
   if (ws_bytes < need) return fail(MCS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (!ws || !aligned16(ws)) return fail(MCS_ERR_INVALID_ARGUMENT, "ws is NULL or not 16-byte aligned");
   return hip_status(mcs::run_pddp((const uint16_t *)q, desc->stride_b, desc->stride_n, desc->stride_h,
                                   desc->batch, desc->heads, desc->seqlen, desc->head_dim, group_size,
-                                  power_iters, perm, ws, ws_bytes, (hipStream_t)stream),
+                                  power_iters, (flags & MCS_PDDP_WHITEN) != 0, perm, ws, ws_bytes,
+                                  (hipStream_t)stream),
                     "mcs_pddp_group");
+}
+
+mcs_status_t mcs_pddp_group(const mcs_attn_desc_t *desc, const void *q, int32_t group_size,
+                            int32_t power_iters, int32_t *perm, void *ws, size_t ws_bytes,
+                            mcs_stream_t stream) {
+  return mcs_pddp_group_ex(desc, q, group_size, power_iters, 0u, perm, ws, ws_bytes, stream);
 }
 
 mcs_status_t mcs_anchor_dense_lse(const mcs_attn_desc_t *desc, const void *q, const void *k,

@@ -46,7 +46,7 @@ hipError_t launch_idx_decode(const uint32_t *bitmap, int64_t rows, int K, int N,
 
 size_t pddp_workspace_bytes(int B, int H, int N, int D, int T);
 hipError_t run_pddp(const uint16_t *q, int64_t sb, int64_t sn, int64_t sh, int B, int H, int N,
-                    int D, int T, int power_iters, int32_t *perm, void *ws, size_t ws_bytes,
-                    hipStream_t s);
+                    int D, int T, int power_iters, bool whiten, int32_t *perm, void *ws,
+                    size_t ws_bytes, hipStream_t s);
 
 }  // namespace mcs

@@ -32,6 +32,12 @@
 //   project  per chunk of a node: p_i = (q_i - mu) . u in float64
 //   split    per node: radix select of the floor(G_S/2)*T-th smallest
 //            (p, position) and a stable partition of the node's range.
+// Whitened grouping (an open item of the authors on the news page; read as
+// per-dimension standardization) runs the same tree on the queries scaled by
+// w_d = 1/sigma_d of the root: every node's covariance becomes w_i C_ij w_j,
+// its direction is reported as w_d u_d in the queries' own coordinates, and
+// the root's start index is the lowest dimension of nonzero variance.
+//
 // All sums run in a fixed order, so the result is bitwise reproducible, and
 // decisions are taken on float64 values so the split does not hinge on fp32
 // rounding. Level 0 needs neither the plan nor perm (its one unit is the
@@ -157,7 +163,7 @@ inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int moment_doubles(int D) { return (D / 16) * (D / 16 + 1) / 2 * 256 + D; }
 
 struct WsLayout {
-  size_t levels, nodes, units, mchunks, pchunks, part, ured, nodem, mu, dir, proj, tmp, total;
+  size_t levels, nodes, units, mchunks, pchunks, part, ured, nodem, mu, dir, proj, tmp, wscale, total;
 };
 
 WsLayout ws_layout(const PlanCounts &pc, int BH, int N, int D) {
@@ -177,6 +183,7 @@ WsLayout ws_layout(const PlanCounts &pc, int BH, int N, int D) {
   w.dir = o; o = align_up(o + sizeof(double) * (size_t)BH * at_least1(pc.max_nodes) * D);
   w.proj = o; o = align_up(o + sizeof(double) * (size_t)BH * N);
   w.tmp = o; o = align_up(o + sizeof(int32_t) * (size_t)BH * N);
+  w.wscale = o; o = align_up(o + sizeof(double) * (size_t)BH * D);
   w.total = o;
   return w;
 }
@@ -200,10 +207,12 @@ struct PddpArgs {
   PUnit *units;
   PChunk *mchunks, *pchunks;
   double *part, *ured, *nodem, *mu, *dir, *proj;
+  double *wscale;  // whitening: per-head 1/sigma_d of the root (1 where sigma_d = 0)
   int32_t *tmp;
   int max_mchunks, max_runits, max_units, max_nodes;
   int level;
   int power_iters;
+  int whiten;
 };
 
 __global__ void init_perm_kernel(int32_t *perm, int N, int64_t total) {
@@ -398,7 +407,7 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
   constexpr int JPP = D / PARTS;    // rows per part
   constexpr int CS = 33;            // row stride (doubles) of the 32-column exchange buffer
   __shared__ double Cb[D * CS];
-  __shared__ double u[D], wpart[PARTS][D], red[4], mvec[D], diag[D];
+  __shared__ double u[D], wpart[PARTS][D], red[4], mvec[D], diag[D], wsc[D];
   __shared__ int jstar;
   const PLevel L = a.levels[a.level];
   const int bh = blockIdx.y;
@@ -469,19 +478,57 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
       a.mu[((int64_t)bh * a.max_nodes + ln) * D + tid] = (double)bf16_to_f32(qh[tid]) + mvec[tid];
     }
     __syncthreads();
-    // start vector: e_j for the largest diagonal entry (lowest j on ties)
-    if (wave == 0) {
-      double v = diag[lane];
-      int j = lane;
-      if (D > 64) {
-        const double v2 = diag[lane + 64];
-        if (v2 > v) {
-          v = v2;
-          j = lane + 64;
+    if (a.whiten) {
+      // per-dimension standardization: the root's variances give
+      // w_d = 1/sigma_d (1 for a zero variance), kept for the deeper levels;
+      // the node's covariance becomes w_i C_ij w_j
+      if (tid < D) {
+        double w;
+        if (a.level == 0) {
+          const double v = diag[tid];
+          w = v > 0.0 ? 1.0 / sqrt(v) : 1.0;
+          a.wscale[(int64_t)bh * D + tid] = w;
+        } else {
+          w = a.wscale[(int64_t)bh * D + tid];
+        }
+        wsc[tid] = w;
+      }
+      __syncthreads();
+      int mw = 0;
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) {
+#pragma unroll
+        for (int bj = bi; bj < NB; ++bj, ++mw) {
+          const int gi = 16 * bi + r, gj = 16 * bj + c;
+          val[mw] *= wsc[gi] * wsc[gj];
+          if (bi == bj && r == c) diag[gi] = val[mw];
         }
       }
-      wave_argmax(v, j);
-      if (lane == 0) jstar = j;
+      __syncthreads();
+    }
+    // start vector: e_j for the largest diagonal entry (lowest j on ties).
+    // Whitened root: every standardized variance is 1 in exact arithmetic,
+    // so the tie rule's answer, the lowest dimension of nonzero variance, is
+    // taken exactly (0 when every variance is 0).
+    if (wave == 0) {
+      if (a.whiten && a.level == 0) {
+        const uint64_t nz0 = __ballot(diag[lane] > 0.0);
+        const uint64_t nz1 = D > 64 ? __ballot(diag[(lane + 64) % D] > 0.0) : 0ull;
+        if (lane == 0) jstar = nz0 ? __ffsll((unsigned long long)nz0) - 1
+                                   : (nz1 ? 64 + __ffsll((unsigned long long)nz1) - 1 : 0);
+      } else {
+        double v = diag[lane];
+        int j = lane;
+        if (D > 64) {
+          const double v2 = diag[lane + 64];
+          if (v2 > v) {
+            v = v2;
+            j = lane + 64;
+          }
+        }
+        wave_argmax(v, j);
+        if (lane == 0) jstar = j;
+      }
     }
     // thread (part, col) keeps rows part, part + PARTS, ... of column col of
     // C in registers for all iterations (C is symmetric: column = row). C
@@ -557,9 +604,11 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
     if (lane == 0) jstar = j;
   }
   __syncthreads();
+  // the direction in the queries' own coordinates (whitened: w_d u_d, so
+  // the projection of x - mu equals that of the standardized queries)
   if (tid < D) {
     const double sgn = (u[jstar] < 0.0) ? -1.0 : 1.0;
-    a.dir[((int64_t)bh * a.max_nodes + ln) * D + tid] = sgn * u[tid];
+    a.dir[((int64_t)bh * a.max_nodes + ln) * D + tid] = sgn * u[tid] * (a.whiten ? wsc[tid] : 1.0);
   }
 }
 
@@ -827,8 +876,8 @@ size_t pddp_workspace_bytes(int B, int H, int N, int D, int T) {
 }
 
 hipError_t run_pddp(const uint16_t *q, int64_t sb, int64_t sn, int64_t sh, int B, int H, int N,
-                    int D, int T, int power_iters, int32_t *perm, void *ws, size_t ws_bytes,
-                    hipStream_t s) {
+                    int D, int T, int power_iters, bool whiten, int32_t *perm, void *ws,
+                    size_t ws_bytes, hipStream_t s) {
   const int BH = B * H;
   const int64_t total = (int64_t)BH * N;
   std::vector<PLevel> hl(kMaxLevels);
@@ -863,6 +912,8 @@ hipError_t run_pddp(const uint16_t *q, int64_t sb, int64_t sn, int64_t sh, int B
   a.dir = (double *)(base + wl.dir);
   a.proj = (double *)(base + wl.proj);
   a.tmp = (int32_t *)(base + wl.tmp);
+  a.wscale = (double *)(base + wl.wscale);
+  a.whiten = whiten ? 1 : 0;
   a.max_mchunks = pc.max_mchunks;
   a.max_runits = pc.max_runits > 0 ? pc.max_runits : 1;
   a.max_units = pc.max_units;

@@ -25,7 +25,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(s[0] for s in B.SIGNATURES) == names
@@ -65,6 +65,9 @@ def test_validation_codes(lib):
     assert lib.mcs_anchor_dense_lse(ctypes.byref(bad_stride), FAKE, FAKE, FAKE, FAKE, None, None) == 1
     assert lib.mcs_pddp_group(ctypes.byref(d), FAKE, 128, 0, FAKE, FAKE, 1 << 30, None) == 1
     assert lib.mcs_pddp_group(ctypes.byref(d), FAKE, 128, 16, FAKE, FAKE, 16, None) == 3
+    assert lib.mcs_pddp_group_ex(ctypes.byref(d), FAKE, 128, 16, 2, FAKE, FAKE, 1 << 30, None) == 1
+    assert b"flag" in lib.mcs_last_error()
+    assert lib.mcs_pddp_group_ex(ctypes.byref(d), FAKE, 128, 16, 1, FAKE, FAKE, 16, None) == 3
     assert lib.mcs_anchor_select_topk(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 128, 10, FAKE, None, FAKE, 16, None) == 3
     assert lib.mcs_residual(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 0, FAKE, None) == 1
 

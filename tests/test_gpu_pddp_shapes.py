@@ -44,3 +44,54 @@ def test_pddp_groups_exact(lib, N, d, T, H):
     for h in range(H):
         want = O.pddp_group(U.head_np(q, 0, h), T)
         assert np.array_equal(got[0, h], want), f"head {h}: groups differ"
+
+
+def _whitened_groups(q, T):
+    dq = q.cuda()
+    B, N, H, d = dq.shape
+    desc = mcs.desc_for(dq)
+    ws = torch.empty(mcs.pddp_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    mcs.pddp_group(dq, T, perm, ws, whiten=True)
+    torch.cuda.synchronize()
+    return perm.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,d,T", [(5000, 64, 64), (4500, 64, 128), (9000, 128, 64), (1000, 128, 128)])
+def test_whitened_pddp_groups_exact(lib, N, d, T):
+    """Whitened grouping (per-dimension standardization) against the oracle."""
+    print(f"\n[whitened pddp N={N} d={d} T={T}]", flush=True)
+    w = synth.small_workload(N, heads=1, head_dim=d, group_size=T, density_pct=15)
+    q = synth.make_qkv(w, seed=N + 3 * d + T)[0]
+    got = _whitened_groups(q, T)
+    assert np.array_equal(got[0, 0], O.pddp_group(U.head_np(q, 0, 0), T, whiten=True))
+
+
+def test_whitened_pddp_full_size_wan480p(lib):
+    """Two heads of the wan480p shape (N = 32760, d = 128, T = 128); the
+    whitened groups also differ from the plain ones."""
+    print("\n[whitened pddp wan480p]", flush=True)
+    w = synth.WORKLOADS["wan480p"]
+    q = synth.make_qkv(w, seed=5)[0]
+    got = _whitened_groups(q, w.group_size)
+    for h in (0, w.heads - 1):
+        qh = U.head_np(q, 0, h)
+        want = O.pddp_group(qh, w.group_size, whiten=True)
+        assert np.array_equal(got[0, h], want), f"head {h}"
+        assert not np.array_equal(want, O.pddp_group(qh, w.group_size))
+
+
+def test_whitened_pddp_constant_dims_and_equal_queries(lib):
+    """Zero-variance dimensions stay unscaled and the root starts at the
+    first dimension of nonzero variance (dim 0 is constant here); with every
+    query equal all variances are 0 and the groups are index order."""
+    print("\n[whitened pddp constant dims]", flush=True)
+    N, d, T = 1500, 64, 64
+    w = synth.small_workload(N, heads=2, head_dim=d, group_size=T, density_pct=15)
+    q = synth.make_qkv(w, seed=31)[0]
+    q[0, :, 0, 0] = 0.75
+    q[0, :, 0, 9] = -2.0
+    q[0, :, 1, :] = q[0, 0, 1, :]
+    got = _whitened_groups(q, T)
+    assert np.array_equal(got[0, 0], O.pddp_group(U.head_np(q, 0, 0), T, whiten=True))
+    assert np.array_equal(got[0, 1], np.arange(N))
