@@ -177,7 +177,7 @@ mcs_status_t mcs_anchor_dense_lse(const mcs_attn_desc_t *desc, const void *q, co
   a.v = (const uint16_t *)v;
   a.out = (uint16_t *)o;
   a.lse = lse;
-  a.rows = 128;
+  a.rows = 256;  // dense tile: 8 waves x 32 rows
   a.G = groups_of(desc, a.rows);
   return hip_status(mcs::launch_attention(mcs::kModeDense, desc->head_dim, a, (hipStream_t)stream),
                     "mcs_anchor_dense_lse");

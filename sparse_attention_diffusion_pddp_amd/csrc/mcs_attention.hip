@@ -3,8 +3,8 @@
 // residual R = O_dense - O_sparse.
 //
 // One workgroup owns one tile of query rows: a PDDP query group (sparse,
-// residual) or a run of consecutive tokens (dense). Each of its waves owns 32
-// query rows. The key loop walks 64-key tiles; a tile's K rows and V rows are
+// residual) or a run of 256 consecutive tokens (dense: eight waves share each
+// K/V tile). Each of its waves owns 32 query rows. The key loop walks 64-key tiles; a tile's K rows and V rows are
 // gathered by index (or read contiguously, dense) with LDS-DMA buffer loads
 // straight into one of two LDS stages (the next tile fills one stage while
 // the current one is consumed), and consumed by v_mfma_f32_32x32x16_bf16:
@@ -43,7 +43,8 @@ struct AttnCfg {
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int D, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW, 2) void attention_kernel(AttnArgs a) {
+// one 8-wave (dense, 256-row) or two 4-wave workgroups per CU
+__global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attention_kernel(AttnArgs a) {
   using C = AttnCfg<D, NW>;
   // two pipeline stages as separate LDS objects, so the compiler can tell
   // the stage being filled by DMA from the one being read
@@ -318,6 +319,11 @@ static hipError_t launch_one(const AttnArgs &a, hipStream_t s) {
 
 template <int MODE>
 static hipError_t launch_mode(int head_dim, const AttnArgs &a, hipStream_t s) {
+  // dense: 256-row tiles, so eight waves share each K/V tile's DMA
+  if constexpr (MODE == kModeDense) {
+    if (head_dim == 128 && a.rows == 256) return launch_one<128, 8, MODE>(a, s);
+    if (head_dim == 64 && a.rows == 256) return launch_one<64, 8, MODE>(a, s);
+  }
   if (head_dim == 128 && a.rows == 128) return launch_one<128, 4, MODE>(a, s);
   if (head_dim == 128 && a.rows == 64) return launch_one<128, 2, MODE>(a, s);
   if (head_dim == 64 && a.rows == 128) return launch_one<64, 4, MODE>(a, s);
