@@ -12,12 +12,15 @@
 // cross-half add; the 4 (or 2) waves' partial sums meet in LDS and are added
 // in a fixed order (no atomics).
 //
-// topk_kernel: one workgroup per (b, h, g). A radix select, most significant
-// digit first, finds the K-th largest mass: the first digit from the whole
-// row, the rest from the first digit's bin compacted into LDS; a single
-// ordered pass with ballot prefix counts then keeps every key above it and
-// the lowest-index keys equal to it, writing their indices in ascending
-// order. Two reads of the row in all.
+// Top-K: one workgroup per (b, h, g). A radix select, most significant
+// digit first, finds the K-th largest mass; an ordered pass with ballot
+// prefix counts then keeps every key above it and the lowest-index keys equal
+// to it, writing their indices in ascending order.
+//   topk_reg_kernel (rows up to 65536 keys): the row is read once into
+//     registers and every digit and the partition work from there;
+//   topk_kernel (longer rows): the first digit from the row, the rest from
+//     that digit's bin compacted into LDS (or from the row again when the
+//     bin does not fit), then the partition reads the row once more.
 #include <type_traits>
 
 #include "mcs_common.hpp"
