@@ -95,3 +95,23 @@ def test_whitened_pddp_constant_dims_and_equal_queries(lib):
     got = _whitened_groups(q, T)
     assert np.array_equal(got[0, 0], O.pddp_group(U.head_np(q, 0, 0), T, whiten=True))
     assert np.array_equal(got[0, 1], np.arange(N))
+
+
+@pytest.mark.parametrize("iters", [1, 3, 64])
+@pytest.mark.parametrize("whiten", [False, True])
+def test_pddp_power_iteration_counts(lib, iters, whiten):
+    """The API's iteration count reaches the kernel. With 1 or 3 iterations
+    the direction is far from converged, so the start vector and every step
+    must match the oracle's."""
+    print(f"\n[pddp iters={iters} whiten={whiten}]", flush=True)
+    N, d, T = 3000, 128, 128
+    w = synth.small_workload(N, heads=1, head_dim=d, group_size=T, density_pct=15)
+    q = synth.make_qkv(w, seed=40 + iters)[0]
+    dq = q.cuda()
+    desc = mcs.desc_for(dq)
+    ws = torch.empty(mcs.pddp_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+    perm = torch.empty((1, 1, N), dtype=torch.int32, device="cuda")
+    mcs.pddp_group(dq, T, perm, ws, power_iters=iters, whiten=whiten)
+    torch.cuda.synchronize()
+    want = O.pddp_group(U.head_np(q, 0, 0), T, power_iters=iters, whiten=whiten)
+    assert np.array_equal(perm.cpu().numpy()[0, 0], want)
