@@ -407,7 +407,7 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
   constexpr int JPP = D / PARTS;    // rows per part
   constexpr int CS = 33;            // row stride (doubles) of the 32-column exchange buffer
   __shared__ double Cb[D * CS];
-  __shared__ double u[D], wpart[PARTS][D], red[4], mvec[D], diag[D], wsc[D];
+  __shared__ double u[D], wpart[PARTS][D], mvec[D], diag[D], wsc[D];
   __shared__ int jstar;
   const PLevel L = a.levels[a.level];
   const int bh = blockIdx.y;
@@ -568,24 +568,32 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
     }
     wpart[part][col] = s0 + s1;
     __syncthreads();
-    double w = 0.0, sq = 0.0;
-    if (tid < D) {
+    // every wave forms all of w and its norm (entry lane + 64 q in lane
+    // order, the same sums in the same order in every wave), so no second
+    // exchange is needed; wave 0 writes the new u
+    double wq[(D + 63) / 64], nrm2 = 0.0;
 #pragma unroll
-      for (int p = 0; p < PARTS; ++p) w += wpart[p][tid];
-      sq = w * w;
+    for (int q = 0; q < (D + 63) / 64; ++q) {
+      double w = 0.0;
+#pragma unroll
+      for (int p = 0; p < PARTS; ++p) w += wpart[p][lane + 64 * q];
+      wq[q] = w;
+      double sq = w * w;
+#pragma unroll
+      for (int s = 32; s > 0; s >>= 1) sq += __shfl_xor(sq, s);
+      nrm2 += sq;
     }
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) sq += __shfl_xor(sq, s);
-    if (lane == 0) red[wave] = sq;
-    __syncthreads();
-    double nrm2 = 0.0;
-#pragma unroll
-    for (int q = 0; q < (D + 63) / 64; ++q) nrm2 += red[q];
     if (nrm2 == 0.0) {  // all queries equal: every projection will be 0
-      if (tid < D) u[tid] = 0.0;
+      if (wave == 0) {
+#pragma unroll
+        for (int q = 0; q < (D + 63) / 64; ++q) u[lane + 64 * q] = 0.0;
+      }
       break;
     }
-    if (tid < D) u[tid] = w / sqrt(nrm2);
+    if (wave == 0) {
+#pragma unroll
+      for (int q = 0; q < (D + 63) / 64; ++q) u[lane + 64 * q] = wq[q] / sqrt(nrm2);
+    }
     __syncthreads();
   }
   __syncthreads();
@@ -747,6 +755,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_reg_kernel(PddpArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t lt_cnt[NW], eq_cnt[NW];
   __shared__ uint32_t sel_digit, sel_below;
+  __shared__ unsigned long long tau_s;
   const PLevel L = a.levels[a.level];
   const int bh = blockIdx.y;
   const PNode nd = a.nodes[L.node0 + blockIdx.x];
@@ -789,6 +798,16 @@ __global__ __launch_bounds__(kSplitThreads) void split_reg_kernel(PddpArgs a) {
     prefix |= (uint64_t)sel_digit << shift;
     mask |= (uint64_t)255 << shift;
     remaining -= sel_below;
+    // a bin holding one key: that key is the threshold (and remaining is 1),
+    // so the low digits need no more passes
+    if (pass < 7 && hist[sel_digit] == 1u) {
+#pragma unroll
+      for (int k = 0; k < KPT; ++k)
+        if ((key[k] & mask) == prefix) tau_s = key[k];
+      __syncthreads();
+      prefix = tau_s;
+      break;
+    }
   }
   const uint64_t tau = prefix;
   const uint32_t need = remaining;
