@@ -480,7 +480,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "the hot path shards by heads with no exchange, and this build measures one GPU's share.",
+              "the hot path shards by heads with no exchange, so the bench measures one GPU's share.",
               file=sys.stderr)
         sys.exit(2)
 

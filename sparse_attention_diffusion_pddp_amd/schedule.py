@@ -1,4 +1,4 @@
-"""Denoising schedule of a layer stack and its driver.
+"""Denoising schedule of a layer stack and its runner.
 
 Appendix Table 9 of the paper landing page gives, per model, the layers
 that always stay dense, the dense warm-up steps and the anchor steps (1-indexed).

@@ -1,4 +1,4 @@
-"""The layer-stack driver on the GPU: with R offloaded to pinned host memory
+"""The layer-stack runner on the GPU: with R offloaded to pinned host memory
 and prefetched one layer ahead on a side stream, every output equals the run
 that keeps R on the device, bitwise; one reuse layer is checked against the
 oracle; the per-kind call counts follow the schedule."""
