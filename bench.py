@@ -45,13 +45,14 @@ def kernel_hash() -> str:
 
 def load_traffic(per_launch_flops):
     """HBM bytes per sparse_apply launch from committed rocprofv3 counters,
-    if they were taken on the current kernel source."""
+    if they were taken on the current kernel source and on a launch of the
+    same work (the counted workload's effective FLOPs)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_hash():
+    if t.get("kernel_hash") != kernel_hash() or t.get("per_launch_flop") != per_launch_flops:
         return None
     return t.get("bytes_per_launch")
 
@@ -86,7 +87,10 @@ def write_traffic(fetch_dir, write_dir, fetch_copy_dir, write_copy_dir, kernel="
     fetch_c, _ = per_dispatch(fetch_copy_dir, "FETCH_SIZE", "copyBuffer")
     write_c, _ = per_dispatch(write_copy_dir, "WRITE_SIZE", "copyBuffer")
     fs, ws = copy_kib / fetch_c, copy_kib / write_c
+    from sparse_attention_diffusion_pddp_amd import metrics, synth
+    w = synth.WORKLOADS["wan480p"]  # the workload of the counted bench runs
     out = {"kernel": f"{kernel} (mcs_sparse_apply), wan480p 15%", "kernel_hash": kernel_hash(),
+           "workload": "wan480p", "per_launch_flop": metrics.sparse_flops(w.batch, w.heads, w.seqlen, w.topk, w.head_dim),
            "dispatches": {"fetch": n_f, "write": n_w},
            "fetch_kib_per_launch": round(fetch, 1), "write_kib_per_launch": round(write, 1),
            "copy_calibration_kib": {"bytes_copied_kib": copy_kib, "fetch_kib": round(fetch_c, 1),

@@ -4,7 +4,8 @@
 //
 // One workgroup owns one tile of query rows: a PDDP query group (sparse,
 // residual) or a run of 256 consecutive tokens (dense: eight waves share each
-// K/V tile). Each of its waves owns 32 query rows. The key loop walks 64-key tiles; a tile's K rows and V rows are
+// K/V tile). Each of its waves owns 32 query rows. The key loop walks 64-key
+// tiles (128-key tiles on the dense path); a tile's K rows and V rows are
 // gathered by index (or read contiguously, dense) with LDS-DMA buffer loads
 // straight into one of two LDS stages (the next tile fills one stage while
 // the current one is consumed), and consumed by v_mfma_f32_32x32x16_bf16:
@@ -25,11 +26,11 @@
 
 namespace mcs {
 
-template <int D, int NW>
+template <int D, int NW, int KT_>
 struct AttnCfg {
   static constexpr int TQ = 32 * NW;           // query rows per workgroup
   static constexpr int NT = 64 * NW;           // threads
-  static constexpr int KT = 64;                // keys per tile
+  static constexpr int KT = KT_;               // keys per tile
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int ROWB = D * 2;           // bytes per K or V row
   static constexpr int TILEB = KT * ROWB;      // bytes of one K (or V) tile
@@ -45,7 +46,11 @@ constexpr float kRescaleLog2 = 8.0f;
 template <int D, int NW, int MODE>
 // one 8-wave (dense, 256-row) or two 4-wave workgroups per CU
 __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attention_kernel(AttnArgs a) {
-  using C = AttnCfg<D, NW>;
+  // 128-key tiles on the 256-row dense path (one barrier and DMA wait per
+  // 128 keys; its single workgroup per CU has the LDS for them), 64 keys
+  // elsewhere
+  using C = AttnCfg<D, NW, (MODE == kModeDense && NW >= 8) ? 128 : 64>;
+  static_assert(MODE == kModeDense || C::KT == 64, "one index per lane of wave 0 covers a tile");
   // two pipeline stages as separate LDS objects, so the compiler can tell
   // the stage being filled by DMA from the one being read
   __shared__ __attribute__((aligned(1024))) bf16_t st0[2 * C::TILEB / 2];
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attention_kernel(Att
     // halves A (keys 0..31) and B (32..63): QK(B) is issued next to A's
     // exponentials and PV(A) next to B's max, so MFMA and VALU work of one
     // wave interleave
-    f32x16 st[2];
+    f32x16 st[C::KT / 32];
     const int grp = lane >> 4, j = lane & 15;
     const int dim = 16 * (grp & 1) + 4 * (j & 3);
     auto qkh = [&](int kb2) {
@@ -222,15 +227,31 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attention_kernel(Att
         }
       }
     };
-    bf16x8 pfa[2], pfb[2];
-    qkh(0);
-    rescale(0);
-    qkh(1);
-    exps(0, pfa);
-    pvh(0, pfa);
-    rescale(1);
-    exps(1, pfb);
-    pvh(1, pfb);
+    if constexpr (C::KT == 64) {
+      bf16x8 pfa[2], pfb[2];
+      qkh(0);
+      rescale(0);
+      qkh(1);
+      exps(0, pfa);
+      pvh(0, pfa);
+      rescale(1);
+      exps(1, pfb);
+      pvh(1, pfb);
+    } else {
+      // the same pairing over four 32-key quarters
+      bf16x8 pf[C::KT / 32][2];
+      qkh(0);
+      rescale(0);
+#pragma unroll
+      for (int k = 1; k < C::KT / 32; ++k) {
+        qkh(k);
+        exps(k - 1, pf[k - 1]);
+        pvh(k - 1, pf[k - 1]);
+        rescale(k);
+      }
+      exps(C::KT / 32 - 1, pf[C::KT / 32 - 1]);
+      pvh(C::KT / 32 - 1, pf[C::KT / 32 - 1]);
+    }
 
     if (!LAST) {
       // idx_s[t&1] (tile t's rows) was last read by issue(t) one tile ago

@@ -49,13 +49,15 @@ def test_write_traffic_scales_by_the_copy(tmp_path, monkeypatch):
     assert t["fetch_scale"] == 2.0 and t["write_scale"] == 1.0
     assert t["bytes_per_launch"] == (2000 * 2 + 500) * 1024
     assert t["kernel_hash"] == bench.kernel_hash()
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
-    assert bench.load_traffic(0) == (2000 * 2 + 500) * 1024
+    # reported only for a launch of the counted work (wan480p at 15%)
+    assert t["workload"] == "wan480p" and t["per_launch_flop"] == 989077340160
+    assert bench.load_traffic(989077340160) == (2000 * 2 + 500) * 1024
+    assert bench.load_traffic(17812571553792) is None  # longvideo's reuse call
 
 
 def test_committed_traffic_is_ignored_once_the_kernel_changes(monkeypatch):
     monkeypatch.setattr(bench, "kernel_hash", lambda: "not-the-hash")
-    assert bench.load_traffic(0) is None
+    assert bench.load_traffic(989077340160) is None
 
 
 @pytest.mark.parametrize("anchors,expect", [
