@@ -65,6 +65,13 @@ enum {
 /* A hipStream_t, kept opaque so this header needs no HIP include. */
 typedef void *mcs_stream_t;
 
+/* Checked by every call (MCS_ERR_INVALID_ARGUMENT unless noted): B, H, N >= 1
+ * with B*H*N <= 2^31-1; N <= 2^28 (else MCS_ERR_UNSUPPORTED); strides
+ * non-negative multiples of 8; rows of the layout disjoint (taking the
+ * dimensions of size > 1 by increasing stride, each stride covers the span
+ * of the dimensions inside it, a d-element row innermost), within 2^56
+ * elements; one head's rows within 4 GiB (MCS_ERR_UNSUPPORTED); scale
+ * finite. */
 typedef struct {
   int32_t batch;    /* B >= 1 */
   int32_t heads;    /* H >= 1 */

@@ -35,15 +35,44 @@ mcs_status_t hip_status(hipError_t e, const char *what) {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // extent in elements of a [B,N,H,d] tensor under the descriptor's strides
+// (check_desc has bounded it, so this does not overflow)
 int64_t extent(const mcs_attn_desc_t *d) {
   return (int64_t)(d->batch - 1) * d->stride_b + (int64_t)(d->seqlen - 1) * d->stride_n +
          (int64_t)(d->heads - 1) * d->stride_h + d->head_dim;
 }
 
 bool overlaps(const void *a, const void *b, int64_t bytes) {
-  const char *x = (const char *)a, *y = (const char *)b;
-  return x < y + bytes && y < x + bytes;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b, n = (uintptr_t)bytes;
+  return x < y + n && y < x + n;
 }
+
+// Rows of a [B,N,H,d] layout do not overlap when, taking the dimensions of
+// size > 1 by increasing stride, each stride is at least the span of the
+// dimensions inside it (a row of d elements innermost). The span is kept
+// below 2^56 elements so the extent arithmetic stays in range.
+bool rows_disjoint(const mcs_attn_desc_t *d, bool *too_large) {
+  struct Dim { int64_t count, stride; } dims[3] = {
+      {d->batch, d->stride_b}, {d->seqlen, d->stride_n}, {d->heads, d->stride_h}};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (dims[j].stride < dims[i].stride) std::swap(dims[i], dims[j]);
+  constexpr int64_t kMaxSpan = (int64_t)1 << 56;
+  int64_t span = d->head_dim;
+  *too_large = false;
+  for (const Dim &x : dims) {
+    if (x.count <= 1) continue;
+    if (x.stride < span) return false;
+    int64_t more;
+    if (__builtin_mul_overflow(x.count - 1, x.stride, &more) || __builtin_add_overflow(span, more, &span) ||
+        span > kMaxSpan) {
+      *too_large = true;
+      return true;
+    }
+  }
+  return true;
+}
+
+constexpr int32_t kMaxSeqlen = 1 << 28;
 
 mcs_status_t check_desc(const mcs_attn_desc_t *d) {
   if (!d) return fail(MCS_ERR_INVALID_ARGUMENT, "desc is NULL");
@@ -52,11 +81,16 @@ mcs_status_t check_desc(const mcs_attn_desc_t *d) {
                 d->batch, d->heads, d->seqlen);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(MCS_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->seqlen > kMaxSeqlen) return fail(MCS_ERR_UNSUPPORTED, "seqlen %d above %d", d->seqlen, kMaxSeqlen);
+  if ((int64_t)d->batch * d->heads > (((int64_t)1 << 31) - 1) / d->seqlen)
+    return fail(MCS_ERR_INVALID_ARGUMENT, "batch*heads*seqlen exceeds 2^31-1");
   if (d->stride_b < 0 || d->stride_n < 0 || d->stride_h < 0 || d->stride_b % 8 || d->stride_n % 8 ||
       d->stride_h % 8)
     return fail(MCS_ERR_INVALID_ARGUMENT, "strides must be non-negative multiples of 8 elements");
-  if ((int64_t)d->batch * d->heads * d->seqlen > ((int64_t)1 << 31) - 1)
-    return fail(MCS_ERR_INVALID_ARGUMENT, "batch*heads*seqlen exceeds 2^31-1");
+  bool too_large;
+  if (!rows_disjoint(d, &too_large))
+    return fail(MCS_ERR_INVALID_ARGUMENT, "strides make rows of the [B,N,H,d] layout overlap");
+  if (too_large) return fail(MCS_ERR_INVALID_ARGUMENT, "strides span more than 2^56 elements");
   if (!std::isfinite(d->scale)) return fail(MCS_ERR_INVALID_ARGUMENT, "scale is not finite");
   // the kernels address one head's rows with 32-bit byte offsets
   if ((int64_t)(d->seqlen - 1) * d->stride_n * 2 + d->head_dim * 2 > (int64_t)UINT32_MAX)

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <new>
 #include <vector>
 
 #include "mcsparse.h"
@@ -79,11 +80,20 @@ mcs_status_t mcs_rcache_create(int32_t n_layers, size_t bytes_per_layer, mcs_rca
   if (n_layers < 1) return fail(MCS_ERR_INVALID_ARGUMENT, "n_layers %d < 1", n_layers);
   if (bytes_per_layer == 0 || bytes_per_layer % 16)
     return fail(MCS_ERR_INVALID_ARGUMENT, "bytes_per_layer must be a positive multiple of 16");
-  mcs_rcache *c = new mcs_rcache();
+  size_t host_bytes;
+  if (__builtin_mul_overflow((size_t)n_layers, bytes_per_layer, &host_bytes))
+    return fail(MCS_ERR_INVALID_ARGUMENT, "n_layers * bytes_per_layer overflows");
+  mcs_rcache *c = new (std::nothrow) mcs_rcache();
+  if (!c) return fail(MCS_ERR_INVALID_ARGUMENT, "out of host memory for the cache state");
   c->n_layers = n_layers;
   c->bytes = bytes_per_layer;
-  c->stored.assign(n_layers, 0);
-  hipError_t e = hipHostMalloc((void **)&c->host, (size_t)n_layers * bytes_per_layer, hipHostMallocDefault);
+  try {
+    c->stored.assign(n_layers, 0);
+  } catch (const std::bad_alloc &) {
+    delete c;
+    return fail(MCS_ERR_INVALID_ARGUMENT, "out of host memory for %d layer flags", n_layers);
+  }
+  hipError_t e = hipHostMalloc((void **)&c->host, host_bytes, hipHostMallocDefault);
   for (int s = 0; s < 2 && e == hipSuccess; ++s) {
     e = hipMalloc(&c->slot[s], bytes_per_layer);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ready[s], hipEventDisableTiming);

@@ -72,6 +72,33 @@ def test_validation_codes(lib):
     assert lib.mcs_residual(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 0, FAKE, None) == 1
 
 
+
+def test_descriptor_layout_checks(lib):
+    """Strided layouts: rows that overlap, strides whose extent overflows and
+    dimensions whose product overflows are rejected before any arithmetic
+    can wrap; a packed-qkv view and a heads-major layout are accepted."""
+    n = ctypes.c_size_t()
+
+    def ws(d):
+        return lib.mcs_pddp_group_workspace_size(ctypes.byref(d), 128, ctypes.byref(n))
+
+    H, N, dd = 12, 32760, 128
+    assert ws(B.Desc(1, H, N, dd, N * 3 * H * dd, 3 * H * dd, dd, 0.1)) == 0  # q of a packed qkv
+    assert ws(B.Desc(2, H, N, dd, H * N * dd, dd, N * dd, 0.1)) == 0  # [B, H, N, d] storage
+    # heads interleaved into one token's row: (n=1, h=0) and (n=0, h=1) share memory
+    assert ws(B.Desc(1, H, N, dd, N * H * dd, dd, dd, 0.1)) == 1
+    assert b"overlap" in lib.mcs_last_error()
+    assert ws(B.Desc(1, H, N, dd, N * H * dd, 0, dd, 0.1)) == 1  # every token on one row
+    big = (1 << 63) - 8
+    assert ws(B.Desc(2, 2, 2, dd, big, big // 2 - 4, dd, 0.1)) == 1
+    assert ws(B.Desc(2, H, N, dd, 1 << 40, H * dd, dd, 0.1)) == 0  # a wide batch stride is fine
+    i32 = (1 << 31) - 1
+    assert ws(B.Desc(i32, i32, 1, dd, 8, 8, 8, 0.1)) == 1
+    assert b"2^31" in lib.mcs_last_error()
+    assert ws(B.Desc(1, 1, i32, dd, 8, dd, 8, 0.1)) == 2
+    assert b"seqlen" in lib.mcs_last_error()
+    assert ws(B.Desc(1, 1, 1, dd, 0, 0, 0, float("inf"))) == 1
+
 def test_workspace_sizes(lib):
     d = desc(H=12, N=32760)
     n = ctypes.c_size_t()
