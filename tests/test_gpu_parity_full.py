@@ -1,12 +1,14 @@
 """GPU parity at the workloads' full sizes and launch configuration.
 
-Three layer shapes, each with all heads, d = 128, groups of 128:
+Four layer shapes, each with all heads, d = 128, groups of 128:
   * wan480p: 12 heads, N = 32760 (21x30x52 grid, last group 120 rows),
     K = 4914 (15%), plus one drifted reuse step;
   * wan720p: 40 heads, N = 75600 (21x45x80, last group 80 rows),
     K = 15120 (20%), reuse on the anchor's own inputs (no drift);
   * longvideo: 24 heads, N = 98304 (24x64x64), K = 14746 (15%), plus one
-    drifted reuse step.
+    drifted reuse step;
+  * voxel3d: 16 heads, N = 64000 (40x40x40 grid, 4x4x4 blocks), K = 9600
+    (15%), plus one drifted reuse step.
 The whole pipeline runs on the GPU exactly as bench.py launches it. The
 oracle then checks:
   * PDDP groups of two full heads, exactly;
@@ -36,6 +38,7 @@ SAMPLES = {
     "wan480p": ((0, 7), (0, 101, -1)),
     "wan720p": ((0, 29), (0, 300, -1)),
     "longvideo": ((0, 17), (0, 500, -1)),
+    "voxel3d": ((0, 11), (0, 250, -1)),
 }
 
 
