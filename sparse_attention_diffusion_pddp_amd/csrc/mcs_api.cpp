@@ -41,9 +41,10 @@ int64_t extent(const mcs_attn_desc_t *d) {
          (int64_t)(d->heads - 1) * d->stride_h + d->head_dim;
 }
 
-bool overlaps(const void *a, const void *b, int64_t bytes) {
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b, n = (uintptr_t)bytes;
-  return x < y + n && y < x + n;
+// [a, a + a_bytes) and [b, b + b_bytes) share a byte
+bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (uintptr_t)b_bytes && y < x + (uintptr_t)a_bytes;
 }
 
 // Rows of a [B,N,H,d] layout do not overlap when, taking the dimensions of
@@ -140,13 +141,27 @@ mcs::AttnArgs attn_args(const mcs_attn_desc_t *d) {
 
 int32_t groups_of(const mcs_attn_desc_t *d, int32_t T) { return (d->seqlen + T - 1) / T; }
 
-mcs_status_t check_out_alias(const mcs_attn_desc_t *d, const void *out, const char *oname,
-                             std::initializer_list<std::pair<const void *, const char *>> ins) {
-  const int64_t bytes = extent(d) * 2;
-  for (const auto &in : ins)
-    if (in.first && overlaps(out, in.first, bytes))
-      return fail(MCS_ERR_INVALID_ARGUMENT, "%s overlaps %s", oname, in.second);
+struct Buf {
+  const void *p;
+  int64_t bytes;
+  const char *name;
+};
+
+// an output must share no byte with any other buffer of the call (NULL
+// entries are skipped)
+mcs_status_t check_disjoint(Buf out, std::initializer_list<Buf> others) {
+  if (!out.p) return ok();
+  for (const Buf &b : others)
+    if (b.p && overlaps(out.p, out.bytes, b.p, b.bytes))
+      return fail(MCS_ERR_INVALID_ARGUMENT, "%s overlaps %s", out.name, b.name);
   return ok();
+}
+
+// byte extents of the call's buffers
+int64_t tensor_bytes(const mcs_attn_desc_t *d) { return extent(d) * 2; }
+int64_t per_token_bytes(const mcs_attn_desc_t *d) { return (int64_t)d->batch * d->heads * d->seqlen * 4; }
+int64_t per_group_bytes(const mcs_attn_desc_t *d, int32_t T, int64_t per_row) {
+  return (int64_t)d->batch * d->heads * groups_of(d, T) * per_row * 4;
 }
 
 }  // namespace
@@ -183,6 +198,9 @@ mcs_status_t mcs_pddp_group_ex(const mcs_attn_desc_t *desc, const void *q, int32
   const size_t need = mcs::pddp_workspace_bytes(desc->batch, desc->heads, desc->seqlen, desc->head_dim, group_size);
   if (ws_bytes < need) return fail(MCS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (!ws || !aligned16(ws)) return fail(MCS_ERR_INVALID_ARGUMENT, "ws is NULL or not 16-byte aligned");
+  const int64_t tb = tensor_bytes(desc), pb = per_token_bytes(desc);
+  MCS_TRY(check_disjoint({perm, pb, "perm"}, {{q, tb, "q"}, {ws, (int64_t)need, "ws"}}));
+  MCS_TRY(check_disjoint({ws, (int64_t)need, "ws"}, {{q, tb, "q"}}));
   return hip_status(mcs::run_pddp((const uint16_t *)q, desc->stride_b, desc->stride_n, desc->stride_h,
                                   desc->batch, desc->heads, desc->seqlen, desc->head_dim, group_size,
                                   power_iters, (flags & MCS_PDDP_WHITEN) != 0, perm, ws, ws_bytes,
@@ -204,7 +222,9 @@ mcs_status_t mcs_anchor_dense_lse(const mcs_attn_desc_t *desc, const void *q, co
   MCS_TRY(check_tensor(v, "v"));
   MCS_TRY(check_tensor(o, "o"));
   if (lse) MCS_TRY(check_ptr(lse, "lse"));
-  MCS_TRY(check_out_alias(desc, o, "o", {{q, "q"}, {k, "k"}, {v, "v"}}));
+  const int64_t tb = tensor_bytes(desc), lb = per_token_bytes(desc);
+  MCS_TRY(check_disjoint({o, tb, "o"}, {{q, tb, "q"}, {k, tb, "k"}, {v, tb, "v"}, {lse, lb, "lse"}}));
+  MCS_TRY(check_disjoint({lse, lb, "lse"}, {{q, tb, "q"}, {k, tb, "k"}, {v, tb, "v"}}));
   mcs::AttnArgs a = attn_args(desc);
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;
@@ -248,6 +268,13 @@ mcs_status_t mcs_anchor_select_topk(const mcs_attn_desc_t *desc, const void *q, 
     MCS_TRY(check_ptr(ws, "ws"));
     mass = (float *)ws;
   }
+  {
+    const int64_t tb = tensor_bytes(desc), lb = per_token_bytes(desc);
+    const int64_t mb = per_group_bytes(desc, group_size, desc->seqlen), ib = per_group_bytes(desc, group_size, topk);
+    MCS_TRY(check_disjoint({mass, mb, group_mass ? "group_mass" : "ws"},
+                           {{q, tb, "q"}, {k, tb, "k"}, {lse, lb, "lse"}, {perm, lb, "perm"}, {kv_idx, ib, "kv_idx"}}));
+    MCS_TRY(check_disjoint({kv_idx, ib, "kv_idx"}, {{q, tb, "q"}, {k, tb, "k"}, {lse, lb, "lse"}, {perm, lb, "perm"}}));
+  }
   mcs::SelectArgs a{};
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;
@@ -281,7 +308,10 @@ mcs_status_t mcs_residual(const mcs_attn_desc_t *desc, const void *q, const void
   MCS_TRY(check_tensor(r, "r"));
   MCS_TRY(check_ptr(perm, "perm"));
   MCS_TRY(check_ptr(kv_idx, "kv_idx"));
-  MCS_TRY(check_out_alias(desc, r, "r", {{q, "q"}, {k, "k"}, {v, "v"}, {o_dense, "o_dense"}}));
+  const int64_t tb = tensor_bytes(desc);
+  MCS_TRY(check_disjoint({r, tb, "r"}, {{q, tb, "q"}, {k, tb, "k"}, {v, tb, "v"}, {o_dense, tb, "o_dense"},
+                                        {perm, per_token_bytes(desc), "perm"},
+                                        {kv_idx, per_group_bytes(desc, group_size, topk), "kv_idx"}}));
   mcs::AttnArgs a = attn_args(desc);
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;
@@ -311,7 +341,10 @@ mcs_status_t mcs_sparse_apply(const mcs_attn_desc_t *desc, const void *q, const 
   if (r) MCS_TRY(check_tensor(r, "r"));
   MCS_TRY(check_ptr(perm, "perm"));
   MCS_TRY(check_ptr(kv_idx, "kv_idx"));
-  MCS_TRY(check_out_alias(desc, o, "o", {{q, "q"}, {k, "k"}, {v, "v"}, {r, "r"}}));
+  const int64_t tb = tensor_bytes(desc);
+  MCS_TRY(check_disjoint({o, tb, "o"}, {{q, tb, "q"}, {k, tb, "k"}, {v, tb, "v"}, {r, tb, "r"},
+                                        {perm, per_token_bytes(desc), "perm"},
+                                        {kv_idx, per_group_bytes(desc, group_size, topk), "kv_idx"}}));
   mcs::AttnArgs a = attn_args(desc);
   a.q = (const uint16_t *)q;
   a.k = (const uint16_t *)k;
@@ -349,8 +382,7 @@ mcs_status_t check_code_args(const mcs_attn_desc_t *desc, int32_t group_size, in
   MCS_TRY(check_ptr(idx, "kv_idx"));
   MCS_TRY(check_ptr(bitmap, "bitmap"));
   const int64_t rows = (int64_t)desc->batch * desc->heads * groups_of(desc, group_size);
-  if (overlaps(idx, bitmap, (int64_t)std::min<int64_t>(rows * topk * 4,
-                                                      rows * (int64_t)mcs::idx_bitmap_words(desc->seqlen) * 4)))
+  if (overlaps(idx, rows * topk * 4, bitmap, rows * (int64_t)mcs::idx_bitmap_words(desc->seqlen) * 4))
     return fail(MCS_ERR_INVALID_ARGUMENT, "kv_idx and bitmap overlap");
   return ok();
 }

@@ -99,6 +99,42 @@ def test_descriptor_layout_checks(lib):
     assert b"seqlen" in lib.mcs_last_error()
     assert ws(B.Desc(1, 1, 1, dd, 0, 0, 0, float("inf"))) == 1
 
+
+def test_outputs_overlapping_other_buffers_are_rejected(lib):
+    """Each output is checked against every other buffer of the call with
+    both buffers' own extents (never dereferenced: validation fails first)."""
+    d = desc()  # B=1, H=2, N=1000, d=128: tensors 512,000 B; per-token arrays 8,000 B
+    base = 1 << 30
+
+    def at(off):
+        return ctypes.c_void_p(base + off)
+
+    q, k, v = at(0), at(1 << 20), at(2 << 20)
+    o, r = at(3 << 20), at(4 << 20)
+    perm, idx = at(5 << 20), at(6 << 20)  # idx: 2 heads x 8 groups x 10 keys x 4 B = 640 B
+    assert lib.mcs_sparse_apply(ctypes.byref(d), q, k, v, perm, 128, idx, 10, r, at((5 << 20) - 16), None) == 1
+    assert b"o overlaps perm" in lib.mcs_last_error()
+    assert lib.mcs_residual(ctypes.byref(d), q, k, v, o, perm, 128, idx, 10, at((6 << 20) - 256 * 1024), None) == 1
+    assert b"r overlaps kv_idx" in lib.mcs_last_error()
+    lse = at(7 << 20)
+    assert lib.mcs_anchor_dense_lse(ctypes.byref(d), q, k, v, o, at((3 << 20) + 4096), None) == 1
+    assert b"overlaps lse" in lib.mcs_last_error()
+    # top-K output inside the mass workspace
+    n = ctypes.c_size_t()
+    assert lib.mcs_anchor_select_topk_workspace_size(ctypes.byref(d), 128, 10, ctypes.byref(n)) == 0
+    ws = at(8 << 20)
+    assert lib.mcs_anchor_select_topk(ctypes.byref(d), q, k, lse, perm, 128, 10, at((8 << 20) + 4096), None, ws,
+                                      n.value, None) == 1
+    assert b"overlaps kv_idx" in lib.mcs_last_error()
+    # PDDP's perm inside its workspace
+    assert lib.mcs_pddp_group_workspace_size(ctypes.byref(d), 128, ctypes.byref(n)) == 0
+    assert lib.mcs_pddp_group(ctypes.byref(d), q, 128, 16, at((8 << 20) + 64), ws, n.value, None) == 1
+    assert b"perm overlaps ws" in lib.mcs_last_error()
+    # a bitmap that starts inside a long index array (the index array is the longer one)
+    big = B.Desc(1, 2, 1000, 128, 1000 * 2 * 128, 2 * 128, 128, 0.088)
+    assert lib.mcs_kv_idx_encode(ctypes.byref(big), 128, idx, 900, at((6 << 20) + 20000), None) == 1
+    assert b"overlap" in lib.mcs_last_error()
+
 def test_workspace_sizes(lib):
     d = desc(H=12, N=32760)
     n = ctypes.c_size_t()
