@@ -106,6 +106,7 @@ const char *mcs_last_error(void);
  *   perm      out, int32 [B][H][N].
  *   ws        device workspace of at least mcs_pddp_group_workspace_size()
  *             bytes; contents are scratch.
+ * perm and ws must not overlap q or each other.
  * ------------------------------------------------------------------------ */
 mcs_status_t mcs_pddp_group_workspace_size(const mcs_attn_desc_t *desc, int32_t group_size,
                                            size_t *bytes);
@@ -137,7 +138,7 @@ mcs_status_t mcs_pddp_group_ex(const mcs_attn_desc_t *desc, const void *q, int32
  *   o   = softmax(scale * q k^T) v, bf16 [B,N,H,d] (round to nearest even).
  *   lse = ln sum_j exp(scale * q_i . k_j), fp32 [B][H][N]; NULL skips it (the
  *         plain dense path, used as the speedup denominator).
- * o must not alias q, k or v.
+ * o and lse must not overlap q, k, v or each other.
  * ------------------------------------------------------------------------ */
 mcs_status_t mcs_anchor_dense_lse(const mcs_attn_desc_t *desc, const void *q, const void *k,
                                   const void *v, void *o, float *lse, mcs_stream_t stream);
@@ -157,6 +158,7 @@ mcs_status_t mcs_anchor_dense_lse(const mcs_attn_desc_t *desc, const void *q, co
  *               workspace may be NULL / 0 bytes.
  *   ws          holds A when group_mass is NULL: at least
  *               mcs_anchor_select_topk_workspace_size() bytes.
+ * kv_idx and A (group_mass or ws) must not overlap any input or each other.
  * ------------------------------------------------------------------------ */
 mcs_status_t mcs_anchor_select_topk_workspace_size(const mcs_attn_desc_t *desc, int32_t group_size,
                                                    int32_t topk, size_t *bytes);
@@ -171,8 +173,8 @@ mcs_status_t mcs_anchor_select_topk(const mcs_attn_desc_t *desc, const void *q, 
  *   O_sparse(i) = sum_{j in S_g} softmax_{S_g}(scale * q_i . k_j) v_j, with
  *   the softmax renormalised over the selected set S_g of i's group;
  *   r = bf16(o_dense - O_sparse), [B,N,H,d], rows by token.
- *   o_dense is the bf16 output of mcs_anchor_dense_lse; r must not alias
- *   any input.
+ *   o_dense is the bf16 output of mcs_anchor_dense_lse; r must not overlap
+ *   any input (tensors, perm, kv_idx).
  * ------------------------------------------------------------------------ */
 mcs_status_t mcs_residual(const mcs_attn_desc_t *desc, const void *q, const void *k, const void *v,
                           const void *o_dense, const int32_t *perm, int32_t group_size,
@@ -183,7 +185,7 @@ mcs_status_t mcs_residual(const mcs_attn_desc_t *desc, const void *q, const void
  * walkthrough page, method step 4: reuse query order, KV indices and R with
  * the current step's Q, K, V; add R to the sparse result).
  *   o = bf16(O_sparse(q, k, v; perm, kv_idx) + r); r may be NULL (plain
- *   sparse attention). o must not alias any input.
+ *   sparse attention). o must not overlap any input (tensors, perm, kv_idx).
  * ------------------------------------------------------------------------ */
 mcs_status_t mcs_sparse_apply(const mcs_attn_desc_t *desc, const void *q, const void *k,
                               const void *v, const int32_t *perm, int32_t group_size,
