@@ -94,6 +94,42 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _dev(t, name, dtype=None, numel=None, contiguous=False):
+    """The library takes bare device pointers and cannot see a tensor's
+    device, dtype or size: check them here, before the call."""
+    if t is None:
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} must hold at least {numel} elements, got {t.numel()}")
+
+
+def _tensors(*named):
+    for name, t in named:
+        _dev(t, name, torch.bfloat16)
+
+
+def _groups(desc: Desc, group_size: int) -> int:
+    return (desc.seqlen + group_size - 1) // group_size
+
+
+def _idx_numel(desc: Desc, group_size: int, topk: int):
+    """Elements of a [B][H][G][topk] index array; None when the library will
+    reject group_size or topk itself (it then reports its own status)."""
+    if group_size not in (64, 128) or not 1 <= topk <= desc.seqlen:
+        return None
+    return desc.batch * desc.heads * _groups(desc, group_size) * topk
+
+
+def _per_token(desc: Desc) -> int:
+    return desc.batch * desc.heads * desc.seqlen
+
+
 def desc_for(q: torch.Tensor, scale: float | None = None) -> Desc:
     """Descriptor of a [B, N, H, d] tensor (d contiguous); k, v, o, r share its strides."""
     if q.dim() != 4:
@@ -133,6 +169,9 @@ PDDP_WHITEN = 1  # MCS_PDDP_WHITEN
 def pddp_group(q, group_size, perm, ws, power_iters=16, desc=None, stream=None, whiten=False):
     lib = load()
     desc = desc or desc_for(q)
+    _tensors(("q", q))
+    _dev(perm, "perm", torch.int32, _per_token(desc), contiguous=True)
+    _dev(ws, "ws", contiguous=True)
     if whiten:
         _check("mcs_pddp_group_ex", lib.mcs_pddp_group_ex(ctypes.byref(desc), _ptr(q), group_size, power_iters,
                                                           PDDP_WHITEN, _ptr(perm), _ptr(ws),
@@ -146,6 +185,8 @@ def anchor_dense_lse(q, k, v, o, lse=None, desc=None, stream=None):
     lib = load()
     _same_layout(q, k, v, o)
     desc = desc or desc_for(q)
+    _tensors(("q", q), ("k", k), ("v", v), ("o", o))
+    _dev(lse, "lse", torch.float32, _per_token(desc), contiguous=True)
     _check("mcs_anchor_dense_lse", lib.mcs_anchor_dense_lse(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                                             _ptr(lse), _stream(stream)))
 
@@ -154,6 +195,13 @@ def anchor_select_topk(q, k, lse, perm, group_size, topk, kv_idx, group_mass=Non
     lib = load()
     _same_layout(q, k)
     desc = desc or desc_for(q)
+    _tensors(("q", q), ("k", k))
+    _dev(lse, "lse", torch.float32, _per_token(desc), contiguous=True)
+    _dev(perm, "perm", torch.int32, _per_token(desc), contiguous=True)
+    _dev(kv_idx, "kv_idx", torch.int32, _idx_numel(desc, group_size, topk), contiguous=True)
+    mass_numel = _idx_numel(desc, group_size, desc.seqlen)
+    _dev(group_mass, "group_mass", torch.float32, mass_numel, contiguous=True)
+    _dev(ws, "ws", contiguous=True)
     wsb = ws.numel() * ws.element_size() if ws is not None else 0
     _check("mcs_anchor_select_topk",
            lib.mcs_anchor_select_topk(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), _ptr(perm), group_size, topk,
@@ -164,6 +212,9 @@ def residual(q, k, v, o_dense, perm, group_size, kv_idx, topk, r, desc=None, str
     lib = load()
     _same_layout(q, k, v, o_dense, r)
     desc = desc or desc_for(q)
+    _tensors(("q", q), ("k", k), ("v", v), ("o_dense", o_dense), ("r", r))
+    _dev(perm, "perm", torch.int32, _per_token(desc), contiguous=True)
+    _dev(kv_idx, "kv_idx", torch.int32, _idx_numel(desc, group_size, topk), contiguous=True)
     _check("mcs_residual", lib.mcs_residual(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o_dense), _ptr(perm),
                                             group_size, _ptr(kv_idx), topk, _ptr(r), _stream(stream)))
 
@@ -172,6 +223,9 @@ def sparse_apply(q, k, v, perm, group_size, kv_idx, topk, r, o, desc=None, strea
     lib = load()
     _same_layout(q, k, v, r, o)
     desc = desc or desc_for(q)
+    _tensors(("q", q), ("k", k), ("v", v), ("r", r), ("o", o))
+    _dev(perm, "perm", torch.int32, _per_token(desc), contiguous=True)
+    _dev(kv_idx, "kv_idx", torch.int32, _idx_numel(desc, group_size, topk), contiguous=True)
     _check("mcs_sparse_apply", lib.mcs_sparse_apply(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(perm),
                                                     group_size, _ptr(kv_idx), topk, _ptr(r), _ptr(o), _stream(stream)))
 
@@ -183,9 +237,18 @@ def kv_idx_bitmap_bytes(desc: Desc, group_size: int) -> int:
     return n.value
 
 
+def _codec_args(desc, group_size, kv_idx, topk, bitmap):
+    _dev(kv_idx, "kv_idx", torch.int32, _idx_numel(desc, group_size, topk), contiguous=True)
+    _dev(bitmap, "bitmap", contiguous=True)
+    if group_size in (64, 128) and (bitmap.element_size() != 4 or
+                                    bitmap.numel() * 4 < kv_idx_bitmap_bytes(desc, group_size)):
+        raise ValueError("bitmap must be a 4-byte tensor of at least kv_idx_bitmap_bytes() bytes")
+
+
 def kv_idx_encode(desc: Desc, group_size, kv_idx, topk, bitmap, stream=None):
     """kv_idx int32 [B][H][G][topk] -> bitmap uint32 [B][H][G][ceil(N/32)] (any 4-byte tensor)."""
     lib = load()
+    _codec_args(desc, group_size, kv_idx, topk, bitmap)
     _check("mcs_kv_idx_encode", lib.mcs_kv_idx_encode(ctypes.byref(desc), group_size, _ptr(kv_idx), topk,
                                                       _ptr(bitmap), _stream(stream)))
 
@@ -193,6 +256,7 @@ def kv_idx_encode(desc: Desc, group_size, kv_idx, topk, bitmap, stream=None):
 def kv_idx_decode(desc: Desc, group_size, bitmap, topk, kv_idx, stream=None):
     """bitmap -> kv_idx, ascending (each row must hold exactly topk set bits)."""
     lib = load()
+    _codec_args(desc, group_size, kv_idx, topk, bitmap)
     _check("mcs_kv_idx_decode", lib.mcs_kv_idx_decode(ctypes.byref(desc), group_size, _ptr(bitmap), topk,
                                                       _ptr(kv_idx), _stream(stream)))
 
@@ -208,6 +272,9 @@ class RCache:
         self.bytes = bytes_per_layer
 
     def store(self, layer: int, src: torch.Tensor, stream=None):
+        _dev(src, "src")
+        if src.numel() * src.element_size() < self.bytes:
+            raise ValueError(f"src holds fewer than the cache's {self.bytes} bytes per layer")
         _check("mcs_rcache_store", self.lib.mcs_rcache_store(self.h, layer, _ptr(src), _stream(stream)))
 
     def prefetch(self, layer: int, stream=None):

@@ -226,17 +226,30 @@ class StackRunner:
 
 
 class _DevicePtr:
-    """Stands in for a bf16 tensor at a raw device address (same shape and
-    strides as ``like``) when passed to the binding."""
+    """Stands in for a device tensor at a raw device address (a cache slot),
+    with the shape, strides and dtype of ``like``, when passed to the
+    binding."""
+
+    is_cuda = True
 
     def __init__(self, ptr, like):
         self._ptr, self.shape, self._stride, self.dtype = ptr, like.shape, like.stride(), like.dtype
+        self._numel, self._esize, self._contig = like.numel(), like.element_size(), like.is_contiguous()
 
     def data_ptr(self):
         return self._ptr
 
     def stride(self, *a):
         return self._stride if not a else self._stride[a[0]]
+
+    def numel(self):
+        return self._numel
+
+    def element_size(self):
+        return self._esize
+
+    def is_contiguous(self):
+        return self._contig
 
 
 def _ev(rec, stream=None):

@@ -135,6 +135,19 @@ def test_outputs_overlapping_other_buffers_are_rejected(lib):
     assert lib.mcs_kv_idx_encode(ctypes.byref(big), 128, idx, 900, at((6 << 20) + 20000), None) == 1
     assert b"overlap" in lib.mcs_last_error()
 
+
+def test_binding_refuses_host_tensors(lib):
+    """The library takes bare pointers; the binding refuses tensors that do
+    not live on the GPU before any call reaches it."""
+    import torch
+    q = torch.zeros((1, 300, 2, 128), dtype=torch.bfloat16)
+    perm = torch.zeros((1, 2, 300), dtype=torch.int32)
+    idx = torch.zeros((1, 2, 3, 10), dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.sparse_apply(q, q, q, perm, 128, idx, 10, None, torch.empty_like(q))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.anchor_dense_lse(q, q, q, torch.empty_like(q))
+
 def test_workspace_sizes(lib):
     d = desc(H=12, N=32760)
     n = ctypes.c_size_t()

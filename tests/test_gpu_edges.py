@@ -186,6 +186,26 @@ def test_error_path_raises(lib):
     assert e.value.status == 2
 
 
+
+def test_binding_checks_buffer_sizes(lib):
+    """Index and statistics buffers of the wrong size, dtype or layout are
+    refused by the binding before a kernel could run past them."""
+    w = synth.small_workload(256, heads=1, head_dim=128, group_size=128, density_pct=10)
+    q, k, v = (t.cuda() for t in synth.make_qkv(w, seed=18))
+    o = torch.empty_like(q)
+    perm = torch.zeros((1, 1, 256), dtype=torch.int32, device="cuda")
+    idx = torch.zeros((1, 1, 2, 26), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="perm"):
+        mcs.sparse_apply(q, k, v, perm[..., :200], 128, idx, 26, None, o)
+    with pytest.raises(ValueError, match="kv_idx"):
+        mcs.sparse_apply(q, k, v, perm, 128, idx[..., :20], 26, None, o)
+    with pytest.raises(ValueError, match="kv_idx"):
+        mcs.sparse_apply(q, k, v, perm, 128, idx.long(), 26, None, o)
+    with pytest.raises(ValueError, match="lse"):
+        mcs.anchor_dense_lse(q, k, v, o, torch.empty((1, 1, 255), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError, match="kv_idx"):
+        mcs.residual(q, k, v, o, perm, 128, idx.transpose(2, 3), 26, torch.empty_like(q))
+
 def test_rcache_round_trip_and_order(lib):
     """R of 3 layers stored to pinned host memory, prefetched one layer ahead
     on a side stream, acquired on the compute stream: bitwise equal."""
