@@ -55,6 +55,8 @@ namespace {
 
 constexpr int kChunk0 = 512;     // tokens per moment chunk at level 0
 constexpr int kChunk = 256;      // tokens per moment chunk below level 0
+constexpr int kChunk0Shift = 9, kChunkShift = 8;
+static_assert((1 << kChunk0Shift) == kChunk0 && (1 << kChunkShift) == kChunk, "chunk sizes are powers of two");
 constexpr int kPChunk = 256;     // tokens per projection chunk
 constexpr int kDirectChunks = 4; // a unit of at most this many chunks is summed by the power kernel
 constexpr int kMaxLevels = 40;
@@ -92,6 +94,10 @@ __host__ __device__ PlanCounts plan_tree(int N, int T, PLevel *lv, PNode *nd, PU
                                          PChunk *pc) {
   PlanCounts k{};
   if (N <= T) return k;
+  // T and the chunk sizes are powers of two: shifts instead of divisions,
+  // which on the GPU are long instruction sequences in a serial walk
+  int tsh = 0;
+  while ((1 << tsh) < T) ++tsh;
   // active nodes (more than T tokens) are appended level by level, so the
   // nodes of one level are contiguous; so are the units; level 0 is the root
   nd[0] = PNode{0, N, 0, 0, 0, -1};
@@ -99,11 +105,12 @@ __host__ __device__ PlanCounts plan_tree(int N, int T, PLevel *lv, PNode *nd, PU
   int lb = 0, le = 1, ub = 0, ue = 1;
   while (lb < le) {
     const int cs = k.levels == 0 ? kChunk0 : kChunk;
+    const int csh = k.levels == 0 ? kChunk0Shift : kChunkShift;
     int nm = 0, most = 0;
     for (int u = ub; u < ue; ++u) {
       PUnit x = un[u];
       x.chunk0 = nm;
-      x.nchunks = (x.n + cs - 1) / cs;
+      x.nchunks = (x.n + cs - 1) >> csh;
       if (mc)
         for (int c = 0; c < x.nchunks; ++c) {
           const int rest = x.n - c * cs;
@@ -117,8 +124,8 @@ __host__ __device__ PlanCounts plan_tree(int N, int T, PLevel *lv, PNode *nd, PU
     for (int i = lb; i < le; ++i) {
       PNode x = nd[i];
       maxn = maxn > x.n ? maxn : x.n;
-      const int G = (x.n + T - 1) / T;
-      x.nl = (G / 2) * T;
+      const int G = (x.n + T - 1) >> tsh;
+      x.nl = (G >> 1) << tsh;
       const int nr = x.n - x.nl;  // nr >= nl: the right child is the larger
       const int npc = (x.n + kPChunk - 1) / kPChunk;
       if (pc)
@@ -155,6 +162,145 @@ __host__ __device__ PlanCounts plan_tree(int N, int T, PLevel *lv, PNode *nd, PU
   k.nodes = le;
   k.units = ue;
   return k;
+}
+
+// Stores of the parallel plan builder, and its per-level sanity check: a
+// checked build (the plan is compared with the serial walk on many shapes)
+// redefines both to bounds-check every store and stop a runaway walk.
+#ifndef MCS_PLAN_STORE
+#define MCS_PLAN_STORE(arr, idx, val) ((arr)[idx] = (val))
+#endif
+#ifndef MCS_PLAN_BAD
+#define MCS_PLAN_BAD(le, ue, level) false
+#endif
+
+// Block-wide exclusive sum of one int per thread of a 256-thread block; the
+// total goes to *total. sh holds 4 ints and is free again on return.
+__device__ __forceinline__ int block_excl_scan(int v, int *total, int *sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int t = sh[w];
+    before += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+__device__ __forceinline__ int block_max(int v, int *sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  const int m = max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+  __syncthreads();
+  return m;
+}
+
+// plan_tree's tables built by a 256-thread block, one level at a time: every
+// unit and node of the level is handled by its own thread, and block scans
+// place their chunks and children exactly where the serial walk puts them
+// (same tables, same order). The lists nd / un may be in LDS or in global
+// memory; counts[0], counts[1] receive the numbers of nodes and units.
+// Requires N > T, T a power of two, and nd / un of 2G + 2 entries.
+__device__ void plan_tree_par(int N, int T, PLevel *lv, PNode *nd, PUnit *un, PChunk *mc, PChunk *pc,
+                              int *counts) {
+  __shared__ int sh[4];
+  const int tid = threadIdx.x;
+  int tsh = 0;
+  while ((1 << tsh) < T) ++tsh;
+  if (tid == 0) {
+    nd[0] = PNode{0, N, 0, 0, 0, -1};
+    un[0] = PUnit{0, N, 0, 0};
+  }
+  __syncthreads();
+  int lb = 0, le = 1, ub = 0, ue = 1, level = 0, mtot = 0, ptot = 0;
+  while (lb < le) {
+    if (MCS_PLAN_BAD(le, ue, level)) break;
+    const int cs = level == 0 ? kChunk0 : kChunk;
+    const int csh = level == 0 ? kChunk0Shift : kChunkShift;
+    int nm = 0, most = 0;
+    for (int base = ub; base < ue; base += 256) {
+      const int u = base + tid;
+      const bool ok = u < ue;
+      PUnit x = ok ? un[u] : PUnit{0, 0, 0, 0};
+      const int nch = ok ? (x.n + cs - 1) >> csh : 0;
+      int tot;
+      const int ex = block_excl_scan(nch, &tot, sh);
+      if (ok) {
+        x.chunk0 = nm + ex;
+        x.nchunks = nch;
+        un[u] = x;
+        for (int c = 0; c < nch; ++c) {
+          const int rest = x.n - c * cs;
+          MCS_PLAN_STORE(mc, mtot + nm + ex + c, (PChunk{u - ub, x.off + c * cs, rest < cs ? rest : cs}));
+        }
+      }
+      most = max(most, block_max(nch, sh));
+      nm += tot;
+    }
+    int np = 0, nu_new = 0, nn_new = 0, maxn = 0;
+    for (int base = lb; base < le; base += 256) {
+      const int i = base + tid;
+      const bool ok = i < le;
+      PNode x = ok ? nd[i] : PNode{0, 0, 0, 0, 0, -1};
+      const int G = (x.n + T - 1) >> tsh;
+      x.nl = (G >> 1) << tsh;
+      const int nr = x.n - x.nl;
+      const int npc = ok ? (x.n + kPChunk - 1) / kPChunk : 0;
+      const int kid = (ok && nr > T) ? 1 : 0;
+      const int left = (kid && x.nl > T) ? 1 : 0;
+      int tp, tu, tn;
+      const int ep = block_excl_scan(npc, &tp, sh);
+      const int eu = block_excl_scan(kid, &tu, sh);
+      const int en = block_excl_scan(kid + left, &tn, sh);
+      const int mx = block_max(ok ? x.n : 0, sh);
+      if (ok) {
+        for (int c = 0; c < npc; ++c) {
+          const int rest = x.n - c * kPChunk;
+          MCS_PLAN_STORE(pc, ptot + np + ep + c, (PChunk{i - lb, x.off + c * kPChunk, rest < kPChunk ? rest : kPChunk}));
+        }
+        x.kid_unit = -1;
+        if (kid) {
+          x.kid_unit = nu_new + eu;
+          MCS_PLAN_STORE(un, ue + x.kid_unit, (PUnit{x.off, x.nl, 0, 0}));
+          int pos = le + nn_new + en;
+          if (left) MCS_PLAN_STORE(nd, pos++, (PNode{x.off, x.nl, 0, x.kid_unit, 0, -1}));
+          MCS_PLAN_STORE(nd, pos, (PNode{x.off + x.nl, nr, 0, x.kid_unit, 1, -1}));
+        }
+        nd[i] = x;
+      }
+      np += tp;
+      nu_new += tu;
+      nn_new += tn;
+      maxn = max(maxn, mx);
+    }
+    if (tid == 0) MCS_PLAN_STORE(lv, level, (PLevel{lb, le - lb, ub, ue - ub, mtot, nm, ptot, np, most > kDirectChunks ? 1 : 0, maxn}));
+    mtot += nm;
+    ptot += np;
+    ++level;
+    lb = le;
+    le += nn_new;
+    ub = ue;
+    ue += nu_new;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    counts[0] = le;
+    counts[1] = ue;
+  }
 }
 
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -213,7 +359,32 @@ struct PddpArgs {
   int level;
   int power_iters;
   int whiten;
+  int plan_in_lds;  // the level-0 plan block keeps its node / unit lists in dynamic LDS
 };
+
+// bytes of the plan's node and unit lists (2G + 2 entries each)
+__host__ __device__ inline size_t plan_list_bytes(int N, int T) {
+  const size_t n = 2 * (size_t)((N + T - 1) / T) + 2;
+  return ((n * sizeof(PNode) + 15) & ~(size_t)15) + n * sizeof(PUnit);
+}
+
+// The level-0 plan block: plan_tree_par on the node and unit lists in LDS
+// (copied out by the whole block at the end) when they fit in the dynamic
+// LDS the launch gave it, else on the global lists.
+__device__ void build_plan(const PddpArgs &a, char *lds) {
+  __shared__ int counts[2];
+  if (!a.plan_in_lds) {
+    plan_tree_par(a.N, a.T, a.levels, a.nodes, a.units, a.mchunks, a.pchunks, counts);
+    return;
+  }
+  const size_t n = 2 * (size_t)((a.N + a.T - 1) / a.T) + 2;
+  PNode *nd = (PNode *)lds;
+  PUnit *un = (PUnit *)(lds + ((n * sizeof(PNode) + 15) & ~(size_t)15));
+  plan_tree_par(a.N, a.T, a.levels, nd, un, a.mchunks, a.pchunks, counts);
+  __syncthreads();
+  for (int i = threadIdx.x; i < counts[0]; i += blockDim.x) a.nodes[i] = nd[i];
+  for (int i = threadIdx.x; i < counts[1]; i += blockDim.x) a.units[i] = un[i];
+}
 
 __global__ void init_perm_kernel(int32_t *perm, int N, int64_t total) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -241,6 +412,7 @@ __global__ __launch_bounds__(256, 2) void moment_kernel(PddpArgs a) {
   constexpr int RPT = SUB / TL;              // staged rows per thread
   static_assert(RPT >= 1 && SUB % TL == 0 && TL <= SUB, "staging shape");
   __shared__ double X[SUB * XS];
+  extern __shared__ __attribute__((aligned(16))) char plan_lds[];  // level 0: the plan's lists
 
   const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -249,7 +421,7 @@ __global__ __launch_bounds__(256, 2) void moment_kernel(PddpArgs a) {
   if (L0) {
     const int nch = (a.N + kChunk0 - 1) / kChunk0;
     if ((int)blockIdx.x == nch) {
-      if (bh == 0 && tid == 0) plan_tree(a.N, a.T, a.levels, a.nodes, a.units, a.mchunks, a.pchunks);
+      if (bh == 0) build_plan(a, plan_lds);
       return;
     }
     off = blockIdx.x * kChunk0;
@@ -875,7 +1047,8 @@ hipError_t run_levels(PddpArgs &a, const PlanCounts &pc, const std::vector<PLeve
     a.level = l;
     const PLevel &L = host_levels[l];
     if (l == 0)  // one more block builds the plan tables
-      hipLaunchKernelGGL((moment_kernel<D, true>), dim3(L.nmchunks + 1, BH), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((moment_kernel<D, true>), dim3(L.nmchunks + 1, BH), dim3(256),
+                         a.plan_in_lds ? plan_list_bytes(a.N, a.T) : 0, s, a);
     else
       hipLaunchKernelGGL((moment_kernel<D, false>), dim3(L.nmchunks, BH), dim3(256), 0, s, a);
     if (L.reduced) hipLaunchKernelGGL(reduce_kernel<D>, dim3(L.nunits * NSL, BH), dim3(256), 0, s, a);
@@ -938,6 +1111,10 @@ hipError_t run_pddp(const uint16_t *q, int64_t sb, int64_t sn, int64_t sh, int B
   a.max_units = pc.max_units;
   a.max_nodes = pc.max_nodes;
   a.power_iters = power_iters;
+  // the level-0 blocks run two per CU (registers), so up to 80 KB of LDS
+  // each, the moment staging buffer included, costs no occupancy
+  const size_t staging = (size_t)32 * (D + 1) * sizeof(double);
+  a.plan_in_lds = plan_list_bytes(N, T) + staging <= (size_t)80 * 1024 ? 1 : 0;
   if (D == 128) return run_levels<128>(a, pc, hl, s);
   return run_levels<64>(a, pc, hl, s);
 }
