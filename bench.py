@@ -120,22 +120,24 @@ def cpu_baseline(w, seconds: float, seed: int):
     perm = O.pddp_group(hq, T)
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    elapsed, flops, groups = 0.0, 0, 0
+    meta = []  # per group of head 0: rows, indices, R (untimed)
     for g in range(w.groups):
         rows = perm[g * T:(g + 1) * T]
         od, L = O.dense_lse(hq[rows], hk, hv, scale)
         idx = O.topk_select(O.group_mass(hq[rows], hk, L, scale), K)
-        R = O.residual(O.round_bf16(od), O.sparse_attention(hq[rows], hk, hv, idx, scale))
-        t0 = time.perf_counter()
-        O.reuse_output(hqt[rows], hkt, hvt, idx, R, scale)
-        elapsed += time.perf_counter() - t0
-        flops += 4 * len(rows) * K * d
-        groups += 1
-        if elapsed >= seconds:
-            break
+        meta.append((rows, idx, O.residual(O.round_bf16(od), O.sparse_attention(hq[rows], hk, hv, idx, scale))))
+    # the timed reuse step over head 0's groups, repeated until `seconds`
+    elapsed, flops, passes = 0.0, 0, 0
+    while elapsed < seconds:
+        for rows, idx, R in meta:
+            t0 = time.perf_counter()
+            O.reuse_output(hqt[rows], hkt, hvt, idx, R, scale)
+            elapsed += time.perf_counter() - t0
+            flops += 4 * len(rows) * K * d
+        passes += 1
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"reuse step of {w.name}: {groups} of {w.groups * w.heads} query groups (head 0), "
-                      f"{elapsed:.1f} s of oracle time, float64 numpy"}
+            "sample": f"reuse step of {w.name}: the {len(meta)} query groups of head 0 (of {w.groups * w.heads}), "
+                      f"{passes} passes, {elapsed:.1f} s of oracle time, float64 numpy"}
 
 
 def input_set(step, anchors):
