@@ -1111,10 +1111,11 @@ hipError_t run_pddp(const uint16_t *q, int64_t sb, int64_t sn, int64_t sh, int B
   a.max_units = pc.max_units;
   a.max_nodes = pc.max_nodes;
   a.power_iters = power_iters;
-  // the level-0 blocks run two per CU (registers), so up to 80 KB of LDS
-  // each, the moment staging buffer included, costs no occupancy
+  // the level-0 blocks run two per CU (registers), so LDS up to half the
+  // CU's 160 KB each, the moment staging buffer included, costs no
+  // occupancy; 72 KB leaves room for allocation granules and small arrays
   const size_t staging = (size_t)32 * (D + 1) * sizeof(double);
-  a.plan_in_lds = plan_list_bytes(N, T) + staging <= (size_t)80 * 1024 ? 1 : 0;
+  a.plan_in_lds = plan_list_bytes(N, T) + staging <= (size_t)72 * 1024 ? 1 : 0;
   if (D == 128) return run_levels<128>(a, pc, hl, s);
   return run_levels<64>(a, pc, hl, s);
 }
