@@ -6,7 +6,9 @@ The full-size tests group at d = 128, T = 128. These cover:
   (10 upper-triangle tiles over 4 waves);
 * T = 64 trees;
 * the reduce pass (units of more than 4 moment chunks) at both widths;
-* register splits of 4-64 keys per thread at d = 64.
+* register splits of 4-64 keys per thread at d = 64;
+* a deep tree (N = 200,000: 11 levels, a root split beyond the register
+  path, the plan's node lists in global memory).
 
 Every head uses the clustered generator of the pages' video workloads."""
 import numpy as np
@@ -26,6 +28,9 @@ SHAPES = [
     (9000, 128, 64, 1),
     (4500, 64, 128, 2),
     (33000, 64, 128, 1),
+    # 11 levels; a root of more than 32,768 tokens (the split's LDS path) and
+    # plan lists too large for the plan block's LDS
+    (200000, 128, 128, 1),
 ]
 
 
