@@ -1,0 +1,52 @@
+"""The oracle and the HIP path share no code: the oracle imports nothing from
+the package, and nothing in the package imports the oracle. Outside tests/,
+only __graft_entry__.smoke() and bench.py's cpu_baseline leg may use it."""
+import ast
+import os
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "sparse_attention_diffusion_pddp_amd")
+
+
+def _imports(path):
+    """(module name, enclosing top-level function or None) for every import."""
+    tree = ast.parse(open(path).read(), path)
+    out = []
+
+    def visit(node, fn):
+        for child in ast.iter_child_nodes(node):
+            f = child.name if isinstance(child, (ast.FunctionDef, ast.AsyncFunctionDef)) and fn is None else fn
+            if isinstance(child, ast.Import):
+                out.extend((a.name, fn) for a in child.names)
+            elif isinstance(child, ast.ImportFrom):
+                out.append(("." * child.level + (child.module or ""), fn))
+            visit(child, f)
+
+    visit(tree, None)
+    return out
+
+
+def _py_files(d):
+    for base, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(".py"):
+                yield os.path.join(base, f)
+
+
+def test_oracle_imports_nothing_from_the_package():
+    for path in _py_files(os.path.join(ROOT, "oracle")):
+        for mod, _ in _imports(path):
+            assert "sparse_attention_diffusion_pddp_amd" not in mod and mod not in ("binding", "synth"), (path, mod)
+
+
+def test_package_does_not_import_the_oracle():
+    for path in _py_files(PKG):
+        for mod, _ in _imports(path):
+            assert not mod.split(".")[0] == "oracle", (path, mod)
+
+
+def test_oracle_use_outside_tests_is_confined():
+    for name, allowed in (("bench.py", {"cpu_baseline"}), ("__graft_entry__.py", {"smoke"})):
+        for mod, fn in _imports(os.path.join(ROOT, name)):
+            if mod.split(".")[0] == "oracle":
+                assert fn in allowed, (name, fn)
