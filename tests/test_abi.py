@@ -148,6 +148,13 @@ def test_binding_refuses_host_tensors(lib):
     with pytest.raises(ValueError, match="GPU tensor"):
         B.anchor_dense_lse(q, q, q, torch.empty_like(q))
 
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback path: without the built library every call raises."""
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.load(str(tmp_path / "libmcsparse.so"))
+
 def test_workspace_sizes(lib):
     d = desc(H=12, N=32760)
     n = ctypes.c_size_t()
