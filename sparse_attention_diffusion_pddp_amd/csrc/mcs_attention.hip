@@ -151,7 +151,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attention_kernel(Att
   // S^T = K Q^T, online softmax, O^T += V^T P^T
   auto tile = [&](int t, const bf16_t *cur, bf16_t *nxt, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
-    if (!LAST) issue(t + 1, nxt);  // rows from idx_s[(t+1)&1]
+    // 128-key tiles: the next tile's DMA first (issuing it later was not
+    // faster there); 64-key tiles issue it after the first half's QK
+    if constexpr (C::KT != 64) {
+      if (!LAST) issue(t + 1, nxt);
+    }
     if (t + 2 < ntiles) fetch_idx(t + 2);
     const bf16_t *ks = cur;
     const bf16_t *vs = cur + C::TILEB / 2;
@@ -230,6 +234,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attention_kernel(Att
     if constexpr (C::KT == 64) {
       bf16x8 pfa[2], pfb[2];
       qkh(0);
+      // the next tile's DMA (rows from idx_s[(t+1)&1]) goes out once the
+      // first half's K reads are issued: its LDS writes then do not compete
+      // with them (2% faster than issuing it first)
+      if (!LAST) issue(t + 1, nxt);
       rescale(0);
       qkh(1);
       exps(0, pfa);
