@@ -23,7 +23,7 @@ Sources (MC-Sparse, arXiv 2610.06801, as summarised on the pages):
     step 4 reuse of query order, KV indices and R with fresh Q/K/V, adding R
     to the sparse result.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * softmax scale s = 1/sqrt(d), no mask;
   * "principal direction" = leading eigenvector of the node's centred
     covariance, from a fixed number of power iterations started at the unit
