@@ -16,7 +16,7 @@
 // digit first, finds the K-th largest mass; an ordered pass with ballot
 // prefix counts then keeps every key above it and the lowest-index keys equal
 // to it, writing their indices in ascending order.
-//   topk_reg_kernel (rows up to 65536 keys): the row is read once into
+//   topk_reg_kernel (rows up to 98304 keys): the row is read once into
 //     registers and every digit and the partition work from there;
 //   topk_kernel (longer rows): the first digit from the row, the rest from
 //     that digit's bin compacted into LDS (or from the row again when the
@@ -475,6 +475,8 @@ hipError_t launch_select(int head_dim, const SelectArgs &a, hipStream_t s) {
   else if (a.N <= 512 * 32) hipLaunchKernelGGL((topk_reg_kernel<512, 32>), grid, dim3(512), 0, s, a);
   else if (a.N <= 512 * 64) hipLaunchKernelGGL((topk_reg_kernel<512, 64>), grid, dim3(512), 0, s, a);
   else if (a.N <= 512 * 128) hipLaunchKernelGGL((topk_reg_kernel<512, 128>), grid, dim3(512), 0, s, a);
+  // 12 waves, three per SIMD: up to 168 VGPRs, room for 128 keys a lane
+  else if (a.N <= 768 * 128) hipLaunchKernelGGL((topk_reg_kernel<768, 128>), grid, dim3(768), 0, s, a);
   else hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -1,8 +1,8 @@
 """Top-K selection at every row length the library dispatches on.
 
-The selection runs differently by row length: rows up to 65536 keys are held
-in registers (four sizes), longer rows compact the first digit's bin into LDS
-when it fits and re-read the row when it does not. The inputs here make the
+The selection runs differently by row length: rows up to 98304 keys are held
+in registers (six sizes, the last on 768 threads), longer rows compact the
+first digit's bin into LDS when it fits and re-read the row when it does not. The inputs here make the
 exact answer plain without the oracle. Every query is c * e_0 and key j is
 k_j * e_0, with k_j on a grid of 257 values, so a group's mass is
 exp(scale * c * k_j - L) summed over identical rows. That is strictly
@@ -47,9 +47,10 @@ def expected(kcol, K):
     return np.sort(order[:K])
 
 
-# register-held rows of 8, 16, 32, 64 and 128 keys per thread; then the long
-# row with the first digit's bin compacted into LDS
-@pytest.mark.parametrize("N", [3000, 8000, 16000, 32760, 60000, 70000])
+# register-held rows of 8, 16, 32, 64 and 128 keys per thread on 512
+# threads, then 128 per thread on 768 threads (70000 and the full 98304);
+# then the long row with the first digit's bin compacted into LDS
+@pytest.mark.parametrize("N", [3000, 8000, 16000, 32760, 60000, 70000, 98304, 100000])
 def test_topk_graded_keys(lib, N):
     print(f"\n[topk graded N={N}]", flush=True)
     rng = np.random.default_rng(N)
@@ -61,9 +62,9 @@ def test_topk_graded_keys(lib, N):
         assert np.array_equal(got[g], want), f"N={N} group {g}"
 
 
-@pytest.mark.parametrize("N", [32760, 70000])
+@pytest.mark.parametrize("N", [32760, 98304, 100000])
 def test_topk_all_masses_tied(lib, N):
-    """Every key equal: the first K indices. At N = 70000 the first digit's
+    """Every key equal: the first K indices. At N = 100000 the first digit's
     bin holds every key, more than LDS keeps, so the row is read again for
     each digit."""
     print(f"\n[topk tied N={N}]", flush=True)
