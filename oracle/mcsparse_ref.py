@@ -68,7 +68,6 @@ __all__ = [
     "sparse_attention",
     "residual",
     "reuse_output",
-    "anchor_head",
 ]
 
 
@@ -262,35 +261,3 @@ def residual(o_dense_stored: np.ndarray, o_sparse: np.ndarray) -> np.ndarray:
 def reuse_output(q_rows, k, v, idx, r_stored, scale) -> np.ndarray:
     """Reuse step: bf16(SparseAttn(fresh Q, K, V; cached idx) + cached R)."""
     return round_bf16(sparse_attention(q_rows, k, v, idx, scale) + r_stored)
-
-
-# ---------------------------------------------------------------------------
-# a whole anchor step for one head
-# ---------------------------------------------------------------------------
-
-def anchor_head(q, k, v, group_size: int, topk: int, scale: float, power_iters: int = 16, groups=None):
-    """Anchor step of one head: PDDP groups, dense O and L, top-K per group and R.
-
-    ``groups`` restricts selection / residual to a list of group ids (all by
-    default). Returns a dict with ``perm``, ``o_dense`` (bf16-rounded),
-    ``lse``, and per selected group ``idx[g]``, ``mass[g]``, ``r[g]``
-    (rows in the group's perm order).
-    """
-    N = q.shape[0]
-    T = group_size
-    perm = pddp_group(q, T, power_iters)
-    G = -(-N // T)
-    groups = range(G) if groups is None else groups
-    out = {"perm": perm, "idx": {}, "mass": {}, "r": {}, "o_dense": {}, "lse": {}}
-    for g in groups:
-        rows = perm[g * T: min((g + 1) * T, N)]
-        o, L = dense_lse(q[rows], k, v, scale)
-        o_st = round_bf16(o)
-        A = group_mass(q[rows], k, L, scale)
-        idx = topk_select(A, topk)
-        out["o_dense"][g] = o_st
-        out["lse"][g] = L
-        out["mass"][g] = A
-        out["idx"][g] = idx
-        out["r"][g] = residual(o_st, sparse_attention(q[rows], k, v, idx, scale))
-    return out

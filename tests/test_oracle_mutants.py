@@ -1,9 +1,12 @@
 """Planted mistakes in the oracle must fail its pins.
 
-Each case swaps one oracle function for a copy with a plausible slip (a
-dropped term, a wrong sign, a transposed operand, an off-by-one count, the
-wrong tie rule) and runs the pin that should catch it. Everything runs on the
-CPU and touches only the oracle.
+numpy oracle: each case swaps one function for a copy with a plausible slip
+(a dropped term, a wrong sign, a transposed operand, an off-by-one count, the
+wrong tie rule) and runs the pin that should catch it.
+
+C++ oracle: the same kinds of slip are compiled into copies of the library
+(ORC_MUTANT = 1..12 in mcsparse_oracle.cpp, one slip each), and each copy
+must fail its pin. Everything runs on the CPU and touches only the oracle.
 """
 import math
 
@@ -56,6 +59,21 @@ def _pd_no_orientation(C, power_iters=16, start=None):
     return -u
 
 
+def _pddp_larger_half_left(q, group_size, power_iters=16, whiten=False):
+    T = int(group_size)
+    out, stack = [], [np.arange(q.shape[0], dtype=np.int64)]
+    while stack:
+        members = stack.pop()
+        G = -(-members.shape[0] // T)
+        if G <= 1:
+            out.append(np.sort(members))
+            continue
+        left, right = ref._split_node(q, members, ((G + 1) // 2) * T, power_iters)  # ceil instead of floor
+        stack.append(right)
+        stack.append(left)
+    return np.concatenate(out)
+
+
 def _sparse_unnormalised(q_rows, k, v, idx, scale):
     ks, vs = k[idx], v[idx]
     s = scale * (q_rows @ ks.T)
@@ -90,6 +108,7 @@ MUTANTS = [
     ("residual", _residual_flipped, pins.test_residual_closed_form_and_anchor_identity),
     ("principal_direction", _pd_15, pins.test_principal_direction_closed_form_iteration_count),
     ("principal_direction", _pd_no_orientation, pins.test_pddp_rank_one_reduces_to_argsort_chunks),
+    ("pddp_group", _pddp_larger_half_left, pins.test_pddp_odd_node_splits_at_floor_half),
     ("sparse_attention", _sparse_unnormalised, pins.test_sparse_decimal_bruteforce),
     ("standardize", _std_unscaled, pins.test_whitened_pddp_root_split_follows_the_correlation_eigenvector),
     ("standardize", _std_by_variance, pins.test_whitened_pddp_root_split_follows_the_correlation_eigenvector),
@@ -103,10 +122,51 @@ def test_pin_catches_planted_mistake(monkeypatch, name, mutant, pin):
     monkeypatch.setattr(ref, name, mutant)
     monkeypatch.setattr(oracle, name, mutant)
     with pytest.raises(AssertionError):
-        pin()
+        pin(ref)
 
 
 def test_pins_pass_unmutated():
     for _, _, pin in MUTANTS:
-        pin()
+        pin(ref)
     assert math.isfinite(1.0)
+
+
+# ORC_MUTANT id -> the pin that must catch it
+CPP_MUTANTS = {
+    1: pins.test_dense_lse_matches_torch_sdpa_and_scipy_logsumexp,   # scale dropped
+    2: pins.test_dense_single_key_and_zero_keys,                     # LSE without its max term
+    3: pins.test_dense_lse_decimal_bruteforce,                       # values paired with the wrong keys
+    4: pins.test_group_mass_decimal_bruteforce_and_row_sums,         # +L instead of -L
+    5: pins.test_topk_tie_rule_and_extremes,                         # ties to the higher index
+    6: pins.test_sparse_decimal_bruteforce,                          # softmax not renormalised
+    7: pins.test_principal_direction_closed_form_iteration_count,    # one power iteration short
+    8: pins.test_pddp_rank_one_reduces_to_argsort_chunks,            # orientation reversed
+    9: pins.test_pddp_odd_node_splits_at_floor_half,                 # ceil(G/2) tiles left
+    10: pins.test_whitened_pddp_root_split_follows_the_correlation_eigenvector,  # never scaled
+    11: pins.test_residual_closed_form_and_anchor_identity,          # sparse - dense
+    12: pins.test_round_bf16_matches_torch_rne,                      # truncation
+}
+
+
+@pytest.fixture(scope="module")
+def cpp_mutants(tmp_path_factory):
+    from oracle import build
+    from oracle.cpp import CppOracle
+    d = tmp_path_factory.mktemp("oracle_mutants")
+    return {m: CppOracle(build.build(mutant=m, out=str(d / f"mutant{m}.so"), verbose=False)) for m in CPP_MUTANTS}
+
+
+@pytest.mark.parametrize("m", sorted(CPP_MUTANTS))
+def test_cpp_pin_catches_planted_mistake(cpp_mutants, m):
+    o = cpp_mutants[m]
+    assert o.mutant == m
+    with pytest.raises(AssertionError):
+        CPP_MUTANTS[m](o)
+
+
+def test_cpp_pins_pass_unmutated():
+    from oracle import cpp
+    o = cpp.default()
+    assert o.mutant == 0
+    for pin in set(CPP_MUTANTS.values()):
+        pin(o)

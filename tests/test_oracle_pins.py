@@ -5,6 +5,11 @@ exact decimal brute force, a library routine (torch SDPA, scipy logsumexp,
 numpy eigh, torch's bf16 conversion, Python's sorted), a closed form, or an
 invariant. A dropped term, a wrong sign, index or transposed operand in the
 oracle fails at least one of them.
+
+Every pin runs twice: on the C++ oracle (``oracle.cpp``, the default export
+of ``oracle``) and on the independent numpy transcription of the same steps
+(``oracle.mcsparse_ref``). A pin is a plain function of the oracle object
+``O`` it checks, so the planted-mistake tests can hand it a mutated one.
 """
 import math
 from decimal import Decimal, getcontext
@@ -14,9 +19,16 @@ import pytest
 import scipy.special
 import torch
 
-import oracle as O
+import oracle.mcsparse_ref as _numpy_oracle
+from oracle import cpp as _cpp
 
 getcontext().prec = 50
+
+
+@pytest.fixture(params=["cpp", "numpy"])
+def O(request):
+    """The oracle implementation under test."""
+    return _cpp.default() if request.param == "cpp" else _numpy_oracle
 
 
 def bf16_values(rng, shape, scale=1.0):
@@ -29,7 +41,7 @@ def bf16_values(rng, shape, scale=1.0):
 # bf16 rounding
 # ---------------------------------------------------------------------------
 
-def test_round_bf16_matches_torch_rne():
+def test_round_bf16_matches_torch_rne(O):
     rng = np.random.default_rng(1)
     x = rng.standard_normal(200000).astype(np.float32) * np.float32(3.0)
     # exact halfway cases between two bf16 neighbours, both parities
@@ -44,7 +56,7 @@ def test_round_bf16_matches_torch_rne():
     np.testing.assert_array_equal(got, want)
 
 
-def test_round_bf16_direct_not_double_rounding():
+def test_round_bf16_direct_not_double_rounding(O):
     # 1 + 2^-8 + 2^-30 lies just above the halfway point between bf16 1.0 and 1+2^-7:
     # rounding straight from float64 gives 1+2^-7; via fp32 it would too, but
     # 1 + 2^-8 exactly is a tie and goes to even (1.0).
@@ -71,7 +83,7 @@ def _decimal_dense(q, k, v, scale):
     return np.array(O_rows), np.array(L)
 
 
-def test_dense_lse_decimal_bruteforce():
+def test_dense_lse_decimal_bruteforce(O):
     rng = np.random.default_rng(2)
     q, k, v = bf16_values(rng, (3, 4)), bf16_values(rng, (6, 4)), bf16_values(rng, (6, 4))
     scale = 1 / math.sqrt(4) * 3.0  # sharpen so the max term matters
@@ -81,7 +93,7 @@ def test_dense_lse_decimal_bruteforce():
     np.testing.assert_allclose(L, L_ref, rtol=0, atol=1e-13)
 
 
-def test_dense_lse_matches_torch_sdpa_and_scipy_logsumexp():
+def test_dense_lse_matches_torch_sdpa_and_scipy_logsumexp(O):
     rng = np.random.default_rng(3)
     q, k, v = bf16_values(rng, (70, 64)), bf16_values(rng, (301, 64)), bf16_values(rng, (301, 64))
     scale = 1 / 8.0
@@ -92,7 +104,7 @@ def test_dense_lse_matches_torch_sdpa_and_scipy_logsumexp():
     np.testing.assert_allclose(L, scipy.special.logsumexp(scale * (q @ k.T), axis=1), rtol=0, atol=1e-12)
 
 
-def test_dense_single_key_and_zero_keys():
+def test_dense_single_key_and_zero_keys(O):
     rng = np.random.default_rng(4)
     q, k, v = bf16_values(rng, (5, 8)), bf16_values(rng, (1, 8)), bf16_values(rng, (1, 8))
     o, L = O.dense_lse(q, k, v, 0.3)
@@ -110,7 +122,7 @@ def test_dense_single_key_and_zero_keys():
 # exact probabilities, group mass, top-K
 # ---------------------------------------------------------------------------
 
-def test_group_mass_decimal_bruteforce_and_row_sums():
+def test_group_mass_decimal_bruteforce_and_row_sums(O):
     rng = np.random.default_rng(5)
     q, k = bf16_values(rng, (4, 4)), bf16_values(rng, (7, 4))
     scale = 0.9
@@ -128,7 +140,7 @@ def test_group_mass_decimal_bruteforce_and_row_sums():
     assert abs(A.sum() - 4.0) < 1e-13  # each row's probabilities sum to one
 
 
-def test_selection_bruteforce_on_tiny_workload():
+def test_selection_bruteforce_on_tiny_workload(O):
     """Tiny workload (1 head, N=1024, d=64, T=64, 25%): the oracle's top-K per
     group equals a brute force with per-row max normalisation (no LSE) and a
     full Python sort by (-A, j)."""
@@ -158,7 +170,7 @@ def test_selection_bruteforce_on_tiny_workload():
         assert np.all(np.diff(got) > 0)
 
 
-def test_topk_tie_rule_and_extremes():
+def test_topk_tie_rule_and_extremes(O):
     A = np.array([0.5, 0.7, 0.5, 0.7, 0.1, 0.5])
     assert O.topk_select(A, 3).tolist() == [0, 1, 3]  # 0.7, 0.7 then the lowest 0.5
     assert O.topk_select(A, 4).tolist() == [0, 1, 2, 3]
@@ -174,7 +186,7 @@ def test_topk_tie_rule_and_extremes():
 # sparse attention, residual, reuse
 # ---------------------------------------------------------------------------
 
-def test_sparse_decimal_bruteforce():
+def test_sparse_decimal_bruteforce(O):
     rng = np.random.default_rng(7)
     q, k, v = bf16_values(rng, (2, 4)), bf16_values(rng, (9, 4)), bf16_values(rng, (9, 4))
     idx = np.array([1, 4, 5, 8])
@@ -183,7 +195,7 @@ def test_sparse_decimal_bruteforce():
     np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
 
 
-def test_sparse_special_cases():
+def test_sparse_special_cases(O):
     rng = np.random.default_rng(8)
     q, k, v = bf16_values(rng, (16, 32)), bf16_values(rng, (50, 32)), bf16_values(rng, (50, 32))
     scale = 1 / math.sqrt(32)
@@ -198,7 +210,7 @@ def test_sparse_special_cases():
                                np.repeat(v[idx].mean(axis=0, keepdims=True), 3, 0), rtol=0, atol=1e-15)
 
 
-def test_residual_closed_form_and_anchor_identity():
+def test_residual_closed_form_and_anchor_identity(O):
     """R_i = (1 - m_i) (Obar_i - O_sparse_i) with m_i the probability mass of the
     selected keys and Obar_i the probability-weighted mean of V over the
     discarded keys; and O_sparse + R reproduces the stored dense output."""
@@ -221,7 +233,7 @@ def test_residual_closed_form_and_anchor_identity():
     assert np.all(np.abs(osp + R_st - od_st) <= np.abs(R_st) * 2**-8 + 1e-300)
 
 
-def test_full_density_residual_vanishes():
+def test_full_density_residual_vanishes(O):
     rng = np.random.default_rng(10)
     q, k, v = bf16_values(rng, (12, 16)), bf16_values(rng, (40, 16)), bf16_values(rng, (40, 16))
     od, _ = O.dense_lse(q, k, v, 0.25)
@@ -232,7 +244,7 @@ def test_full_density_residual_vanishes():
     assert np.all(np.abs(O.residual(od_st, osp)) <= np.abs(od) * 2**-8 + 1e-14)
 
 
-def test_reuse_zero_drift_returns_dense():
+def test_reuse_zero_drift_returns_dense(O):
     rng = np.random.default_rng(11)
     q, k, v = bf16_values(rng, (32, 16)), bf16_values(rng, (64, 16)), bf16_values(rng, (64, 16))
     idx = np.sort(rng.choice(64, 10, replace=False))
@@ -261,14 +273,14 @@ def _check_perm(perm, N, T):
 
 
 @pytest.mark.parametrize("N,T", [(1000, 64), (3 * 64 + 5, 64), (64, 64), (1, 64), (5 * 128, 128), (777, 128)])
-def test_pddp_is_a_tiled_bijection(N, T):
+def test_pddp_is_a_tiled_bijection(O, N, T):
     rng = np.random.default_rng(N)
     q = bf16_values(rng, (N, 16))
     perm = O.pddp_group(q, T)
     _check_perm(perm, N, T)
 
 
-def test_pddp_rank_one_reduces_to_argsort_chunks():
+def test_pddp_rank_one_reduces_to_argsort_chunks(O):
     """q_i = a_i w: every node's direction is +-w/|w| oriented by the largest
     |w_j| (here negative), so the groups are consecutive T-chunks of the
     tokens sorted by (sign * a_i, i)."""
@@ -285,7 +297,7 @@ def test_pddp_rank_one_reduces_to_argsort_chunks():
         assert perm[g * T: (g + 1) * T].tolist() == want
 
 
-def test_pddp_two_separated_clusters_split_exactly():
+def test_pddp_two_separated_clusters_split_exactly(O):
     rng = np.random.default_rng(13)
     T, d = 64, 8
     c = np.zeros(d)
@@ -298,7 +310,25 @@ def test_pddp_two_separated_clusters_split_exactly():
     assert sorted(perm[T:].tolist()) == sorted(np.nonzero(lab == 1)[0].tolist())
 
 
-def test_principal_direction_closed_form_iteration_count():
+def test_pddp_odd_node_splits_at_floor_half(O):
+    """A node of three tiles (G_S = 3) puts floor(3/2) = 1 tile left. Three
+    tight clusters of T tokens: A far out on dim 0, B and C together on
+    dim 0 but apart on dim 1. The root's direction is dim 0, so its lowest
+    tile (A) goes left; the right child's direction is dim 1, which then
+    separates B from C. Two tiles left instead would put A with half of B
+    and C mixed, and the groups would no longer be the clusters."""
+    rng = np.random.default_rng(16)
+    T, d = 64, 4
+    centres = np.array([[-20.0, 0.0, 0, 0], [10.0, -3.0, 0, 0], [10.0, 3.0, 0, 0]])
+    lab = rng.permutation(np.repeat(np.arange(3), T))
+    q = centres[lab] + bf16_values(rng, (3 * T, d), 0.05)
+    perm = O.pddp_group(q, T)
+    groups = [sorted(perm[g * T:(g + 1) * T].tolist()) for g in range(3)]
+    want = [sorted(np.nonzero(lab == c)[0].tolist()) for c in range(3)]
+    assert groups == want
+
+
+def test_principal_direction_closed_form_iteration_count(O):
     """C = [[2,1],[1,2]] (+ zero block): diagonal tie -> start e_0, and
     C^k e_0 = ((3^k + 1)/2, (3^k - 1)/2): the result pins the start, the count
     of 16 iterations and the normalisation."""
@@ -313,7 +343,7 @@ def test_principal_direction_closed_form_iteration_count():
     assert abs(u15[1] - u16[1]) > 1e-9
 
 
-def test_principal_direction_matches_eigh_with_gap():
+def test_principal_direction_matches_eigh_with_gap(O):
     rng = np.random.default_rng(14)
     d = 32
     Qm, _ = np.linalg.qr(rng.standard_normal((d, d)))
@@ -328,17 +358,17 @@ def test_principal_direction_matches_eigh_with_gap():
     assert u[np.argmax(np.abs(u))] > 0
 
 
-def test_principal_direction_zero_covariance():
+def test_principal_direction_zero_covariance(O):
     assert np.all(O.principal_direction(np.zeros((5, 5)), 16) == 0)
 
 
-def test_pddp_equal_queries_fall_back_to_index_order():
+def test_pddp_equal_queries_fall_back_to_index_order(O):
     q = np.ones((300, 8)) * 0.375
     perm = O.pddp_group(q, 64)
     assert perm.tolist() == list(range(300))
 
 
-def test_pddp_first_split_is_median_of_projection():
+def test_pddp_first_split_is_median_of_projection(O):
     """Even G_S: the first split puts exactly the tokens below the projection
     median (on the top eigenvector of the centred covariance, via eigh) left."""
     rng = np.random.default_rng(15)
@@ -370,7 +400,7 @@ def _three_factor_queries(rng, N):
     return q, a, b, c
 
 
-def test_whitened_pddp_root_split_follows_the_correlation_eigenvector():
+def test_whitened_pddp_root_split_follows_the_correlation_eigenvector(O):
     """Whitening (per-dimension standardization): the root split puts left the
     tokens below the median projection on the top eigenvector of the
     correlation matrix (numpy's eigh), the b factor here. The plain split
@@ -396,7 +426,7 @@ def test_whitened_pddp_root_split_follows_the_correlation_eigenvector():
     assert len(plain & set(want)) < 1.6 * T  # a and b are independent
 
 
-def test_whitened_pddp_is_exactly_invariant_to_power_of_two_dim_scaling():
+def test_whitened_pddp_is_exactly_invariant_to_power_of_two_dim_scaling(O):
     """Scaling one dimension by 4 (or 1/4) is exact in floating point, and
     standardization removes it exactly, so the whitened groups are bitwise
     the same. The plain groups are not invariant: the same scaling changes
@@ -411,7 +441,7 @@ def test_whitened_pddp_is_exactly_invariant_to_power_of_two_dim_scaling():
     assert not np.array_equal(O.pddp_group(q, 64), O.pddp_group(q2, 64))
 
 
-def test_standardize_closed_form_and_constant_dims():
+def test_standardize_closed_form_and_constant_dims(O):
     q = np.array([[1.0, 5.0, 2.0], [3.0, 5.0, 2.0], [5.0, 5.0, 8.0], [7.0, 5.0, 8.0]])
     z, var = O.standardize(q)
     # dim 0: mean 4, variance 5; dim 1 constant: variance 0, left unscaled (all 0);
@@ -426,7 +456,7 @@ def test_standardize_closed_form_and_constant_dims():
     _check_perm(perm, 160, 32)
 
 
-def test_topk_count_integer_ceil():
+def test_topk_count_integer_ceil(O):
     assert O.topk_count(25, 1024) == 256
     assert O.topk_count(15, 32760) == 4914
     assert O.topk_count(25, 32760) == 8190
