@@ -2,7 +2,8 @@
 
 Four layer shapes, each with all heads, d = 128, groups of 128:
   * wan480p: 12 heads, N = 32760 (21x30x52 grid, last group 120 rows),
-    K = 4914 (15%), plus one drifted reuse step;
+    K = 4914 (15%), plus one drifted reuse step; and the same layer at
+    25% (K = 8190), the config's second density;
   * wan720p: 40 heads, N = 75600 (21x45x80, last group 80 rows),
     K = 15120 (20%), reuse on the anchor's own inputs (no drift);
   * longvideo: 24 heads, N = 98304 (24x64x64), K = 14746 (15%), plus one
@@ -33,22 +34,27 @@ from tests import parity_util as U
 
 pytestmark = pytest.mark.gpu
 
-# workload: (sampled heads, sampled groups; -1 = the last, possibly short, group)
+# case: (workload, density override or None, sampled heads, sampled groups;
+# -1 = the last, possibly short, group)
 SAMPLES = {
-    "wan480p": ((0, 7), (0, 101, -1)),
-    "wan720p": ((0, 29), (0, 300, -1)),
-    "longvideo": ((0, 17), (0, 500, -1)),
-    "voxel3d": ((0, 11), (0, 250, -1)),
+    "wan480p": ("wan480p", None, (0, 7), (0, 101, -1)),
+    # the same layer at the config's second density (K = 8190)
+    "wan480p@25": ("wan480p", 25, (3, 11), (0, 160, -1)),
+    "wan720p": ("wan720p", None, (0, 29), (0, 300, -1)),
+    "longvideo": ("longvideo", None, (0, 17), (0, 500, -1)),
+    "voxel3d": ("voxel3d", None, (0, 11), (0, 250, -1)),
 }
 
 
 @pytest.fixture(scope="module", params=list(SAMPLES))
 def run(request, lib):
     name = request.param
-    w = synth.WORKLOADS[name]
+    wname, pct, HEADS, GROUPS = SAMPLES[name]
+    w = synth.WORKLOADS[wname]
+    if pct is not None:
+        w = w.with_density(pct)
     B, H, N, d, T, K, G = w.batch, w.heads, w.seqlen, w.head_dim, w.group_size, w.topk, w.groups
-    HEADS = SAMPLES[name][0]
-    GROUPS = tuple(g % G for g in SAMPLES[name][1])
+    GROUPS = tuple(g % G for g in GROUPS)
     print(f"\n[{name} full size: H={H} N={N} d={d} T={T} K={K}]", flush=True)
     q, k, v = synth.make_qkv(w, seed=3)
     if w.drift > 0:

@@ -214,10 +214,35 @@ def test_end_to_end_pipeline_matches_oracle(c, lib):
     assert np.array_equal(perm.cpu().numpy()[0], c.perm)
     gi = idx.cpu().numpy()[0]
     swaps = sum(U.audit_topk(gi[h, g], c.idx[h, g], c.mass[h, g], c.K, c.N) for h in range(c.H) for g in range(c.G))
+    print(f"near-tie swaps: {swaps}")
     got = ot.cpu().float().numpy()[0]
+    got_r = r.cpu().float().numpy()[0]
+    got_od = o.cpu().float().numpy()[0]
     for h in range(c.H):
-        if swaps == 0:
-            U.assert_close(got[:, h], c.o_reuse[:, h], f"end-to-end O_t h{h}")
+        # the oracle's chain, run on the GPU's own (audited) index rows: where
+        # they equal the oracle's (no near-tie swap) this is the oracle's own
+        # end-to-end result, and otherwise each stage is still checked on the
+        # inputs the GPU stage actually had
+        q_, k_, v_ = (U.head_np(t, 0, h) for t in (c.q, c.k, c.v))
+        qt_, kt_, vt_ = (U.head_np(t, 0, h) for t in (c.qt, c.kt, c.vt))
+        want_r = np.zeros((c.N, c.d))
+        want_ot = np.zeros((c.N, c.d))
+        iso_r = np.zeros((c.N, c.d))
+        iso_ot = np.zeros((c.N, c.d))
+        for g in range(c.G):
+            rows = c.perm[h, g * c.T:(g + 1) * c.T]
+            sel = gi[h, g].astype(np.int64)
+            osp = O.sparse_attention(q_[rows], k_, v_, sel, c.scale)
+            want_r[rows] = O.residual(c.o_dense[rows, h], osp)
+            want_ot[rows] = O.reuse_output(qt_[rows], kt_, vt_, sel, want_r[rows], c.scale)
+            # stage isolation: the GPU's own O_dense into the residual, the
+            # GPU's own R into the reuse step
+            iso_r[rows] = O.residual(got_od[rows, h], osp)
+            iso_ot[rows] = O.reuse_output(qt_[rows], kt_, vt_, sel, got_r[rows, h], c.scale)
+        U.assert_close_residual(got_r[:, h], want_r, c.o_dense[:, h], f"end-to-end R h{h}")
+        U.assert_close_chained_reuse(got[:, h], want_ot, want_r, f"end-to-end O_t h{h}")
+        U.assert_close_residual(got_r[:, h], iso_r, got_od[:, h], f"stage-isolated R h{h}")
+        U.assert_close(got[:, h], iso_ot, f"stage-isolated O_t h{h}")
     # the anchor identity on the GPU: sparse + R reproduces the dense output
     o_anchor = torch.empty_like(q)
     mcs.sparse_apply(q, k, v, perm, c.T, idx, c.K, r, o_anchor)
