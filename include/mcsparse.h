@@ -217,18 +217,24 @@ mcs_status_t mcs_kv_idx_decode(const mcs_attn_desc_t *desc, int32_t group_size, 
 /* ------------------------------------------------------------------------
  * Step 5: host offload of cached metadata with a one-layer-ahead prefetch
  * (research walkthrough page, method step 5; paper landing page, Table 8).
- * A cache holds `n_layers` blobs of `bytes_per_layer` bytes in pinned host
- * memory and owns two device slots used in turn (layer l uses slot l % 2),
- * plus the events that order them. It allocates (hipHostMalloc, hipMalloc)
+ * A cache holds `n_layers` (1..65536) blobs of `bytes_per_layer` bytes in
+ * pinned host memory and owns two device slots used in turn (layer l uses
+ * slot l % 2), plus the events that order them (two per layer, two per slot). It allocates (hipHostMalloc, hipMalloc)
  * in create and frees in destroy (which synchronises the device).
  *   store(l, src, s):     D2H copy of `bytes_per_layer` bytes from device
  *                         `src` into layer l's host blob, enqueued on s.
+ *                         It first waits for the last prefetch of layer l,
+ *                         on whatever stream that ran, so the blob is not
+ *                         overwritten while it is being uploaded.
  *   prefetch(l, s):       H2D copy of layer l's blob into slot l % 2 on s
- *                         (a side stream). If the slot was acquired since
- *                         its last prefetch, the copy first waits for all
- *                         work enqueued so far on the acquiring stream, so
- *                         enqueue the slot's reader kernels before the next
- *                         prefetch into that slot.
+ *                         (a side stream). It first waits for the last store
+ *                         of layer l, on whatever stream that ran, so a
+ *                         store and a prefetch of one layer may be enqueued
+ *                         on different streams. If the slot was acquired
+ *                         since its last prefetch, the copy also waits for
+ *                         all work enqueued so far on the acquiring stream,
+ *                         so enqueue the slot's reader kernels before the
+ *                         next prefetch into that slot.
  *   acquire(l, s, &ptr):  makes stream s (the compute stream) wait for the
  *                         prefetch of layer l and returns the slot pointer,
  *                         valid until the next prefetch into the same slot.

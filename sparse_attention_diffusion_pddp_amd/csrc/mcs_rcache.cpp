@@ -29,9 +29,17 @@ struct mcs_rcache {
   bool acquired[2] = {false, false};          // the slot has a reader since its last prefetch
   int32_t slot_layer[2] = {-1, -1};
   std::vector<char> stored;
+  // per layer: the last store's D2H copy into the blob finished, and the
+  // last prefetch's H2D copy out of the blob finished. A prefetch waits for
+  // the first and a store for the second, so the two may run on any streams.
+  std::vector<hipEvent_t> store_done, fetch_done;
+  std::vector<char> fetch_pending;
 };
 
 namespace {
+
+// two events per layer order stores against prefetches
+constexpr int32_t kMaxLayers = 1 << 16;
 
 mcs_status_t fail(mcs_status_t st, const char *fmt, ...) {
   char buf[512];
@@ -61,6 +69,10 @@ mcs_status_t check_layer(const mcs_rcache *c, int32_t layer) {
 }
 
 void release(mcs_rcache *c) {
+  for (hipEvent_t e : c->store_done)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->fetch_done)
+    if (e) (void)hipEventDestroy(e);
   for (int s = 0; s < 2; ++s) {
     if (c->ready[s]) (void)hipEventDestroy(c->ready[s]);
     if (c->freed[s]) (void)hipEventDestroy(c->freed[s]);
@@ -77,7 +89,8 @@ extern "C" {
 mcs_status_t mcs_rcache_create(int32_t n_layers, size_t bytes_per_layer, mcs_rcache_t **out) {
   if (!out) return fail(MCS_ERR_INVALID_ARGUMENT, "out is NULL");
   *out = nullptr;
-  if (n_layers < 1) return fail(MCS_ERR_INVALID_ARGUMENT, "n_layers %d < 1", n_layers);
+  if (n_layers < 1 || n_layers > kMaxLayers)
+    return fail(MCS_ERR_INVALID_ARGUMENT, "n_layers %d outside [1, %d]", n_layers, kMaxLayers);
   if (bytes_per_layer == 0 || bytes_per_layer % 16)
     return fail(MCS_ERR_INVALID_ARGUMENT, "bytes_per_layer must be a positive multiple of 16");
   size_t host_bytes;
@@ -89,11 +102,18 @@ mcs_status_t mcs_rcache_create(int32_t n_layers, size_t bytes_per_layer, mcs_rca
   c->bytes = bytes_per_layer;
   try {
     c->stored.assign(n_layers, 0);
+    c->fetch_pending.assign(n_layers, 0);
+    c->store_done.assign(n_layers, nullptr);
+    c->fetch_done.assign(n_layers, nullptr);
   } catch (const std::bad_alloc &) {
     delete c;
     return fail(MCS_ERR_INVALID_ARGUMENT, "out of host memory for %d layer flags", n_layers);
   }
   hipError_t e = hipHostMalloc((void **)&c->host, host_bytes, hipHostMallocDefault);
+  for (int32_t l = 0; l < n_layers && e == hipSuccess; ++l) {
+    e = hipEventCreateWithFlags(&c->store_done[l], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->fetch_done[l], hipEventDisableTiming);
+  }
   for (int s = 0; s < 2 && e == hipSuccess; ++s) {
     e = hipMalloc(&c->slot[s], bytes_per_layer);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ready[s], hipEventDisableTiming);
@@ -111,9 +131,13 @@ mcs_status_t mcs_rcache_store(mcs_rcache_t *c, int32_t layer, const void *src, m
   const mcs_status_t st = check_layer(c, layer);
   if (st != MCS_OK) return st;
   if (!src) return fail(MCS_ERR_INVALID_ARGUMENT, "src is NULL");
+  // a prefetch of this layer may still be reading the blob
+  if (c->fetch_pending[layer])
+    HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, c->fetch_done[layer], 0), "mcs_rcache_store");
   HIP_TRY(hipMemcpyAsync(c->host + (size_t)layer * c->bytes, src, c->bytes, hipMemcpyDeviceToHost,
                          (hipStream_t)stream),
           "mcs_rcache_store");
+  HIP_TRY(hipEventRecord(c->store_done[layer], (hipStream_t)stream), "mcs_rcache_store");
   c->stored[layer] = 1;
   return MCS_OK;
 }
@@ -130,10 +154,14 @@ mcs_status_t mcs_rcache_prefetch(mcs_rcache_t *c, int32_t layer, mcs_stream_t st
     HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, c->freed[s], 0), "mcs_rcache_prefetch");
     c->acquired[s] = false;
   }
+  // the blob's last store has landed in host memory
+  HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, c->store_done[layer], 0), "mcs_rcache_prefetch");
   HIP_TRY(hipMemcpyAsync(c->slot[s], c->host + (size_t)layer * c->bytes, c->bytes, hipMemcpyHostToDevice,
                          (hipStream_t)stream),
           "mcs_rcache_prefetch");
   HIP_TRY(hipEventRecord(c->ready[s], (hipStream_t)stream), "mcs_rcache_prefetch");
+  HIP_TRY(hipEventRecord(c->fetch_done[layer], (hipStream_t)stream), "mcs_rcache_prefetch");
+  c->fetch_pending[layer] = 1;
   c->slot_layer[s] = layer;
   return MCS_OK;
 }

@@ -359,14 +359,17 @@ __global__ __launch_bounds__(NTH) void topk_reg_kernel(SelectArgs a) {
   // Masses are sums of exponentials, so every key of the row has bit 31 set
   // (a negative value, which cannot occur, would rank as +0). Slots past the
   // row hold key 0: no digit prefix matches it and it is never above the
-  // threshold, so no per-key validity test is needed. Buffer loads: one
-  // offset register for all keys, and reads past the row return 0.
+  // threshold, so no per-key validity test is needed. Buffer loads: the
+  // whole byte offset of key j0 + 64 k is in the VGPR offset (the range check
+  // covers the VGPR and instruction offsets, not the SGPR offset), so a read
+  // past the row's N keys returns 0 and never touches memory after it.
   const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(A, (uint32_t)N * 4u);
   const int nv = N - j0 <= 0 ? 0 : (N - j0 + 63) / 64;  // valid keys of this lane
   uint32_t u[KPT];
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
-    const uint32_t key = order_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, (uint32_t)j0 * 4u, 256 * k, 0)));
+    const uint32_t voff = (uint32_t)(j0 + 64 * k) * 4u;
+    const uint32_t key = order_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, voff, 0, 0)));
     u[k] = k < nv ? (key > 0x80000000u ? key : 0x80000000u) : 0u;
   }
 

@@ -73,3 +73,44 @@ def test_topk_all_masses_tied(lib, N):
     want = np.arange(K)
     for g in range(got.shape[0]):
         assert np.array_equal(got[g], want), f"N={N} group {g}"
+
+
+# one key past a whole number of the register kernel's per-wave segments
+# (64 lanes x keys per lane), so the last wave holds a single valid key; the
+# mass rows sit in a buffer of exactly G * N * 4 bytes from hipMalloc
+@pytest.mark.parametrize("N", [7 * 64 * 8 + 1, 7 * 64 * 16 + 1, 4 * 64 * 32 + 1, 8 * 64 * 128 + 1])
+def test_topk_row_one_past_segments_exact_buffer(lib, N):
+    import ctypes
+    print(f"\n[topk exact buffer N={N}]", flush=True)
+    rng = np.random.default_rng(N)
+    kcol = rng.integers(-128, 129, size=N).astype(np.float64) / 32.0
+    K = (15 * N + 99) // 100
+    q = torch.zeros((1, N, 1, D), dtype=torch.bfloat16)
+    q[0, :, 0, 0] = 2.0
+    k = torch.zeros((1, N, 1, D), dtype=torch.bfloat16)
+    k[0, :, 0, 0] = torch.from_numpy(kcol).to(torch.bfloat16)
+    q, k = q.cuda(), k.cuda()
+    G = -(-N // T)
+    lse = torch.zeros((1, 1, N), dtype=torch.float32, device="cuda")
+    perm = torch.arange(N, dtype=torch.int32, device="cuda").reshape(1, 1, N)
+    idx = torch.empty((1, 1, G, K), dtype=torch.int32, device="cuda")
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    hip.hipFree.argtypes = [ctypes.c_void_p]
+    mass = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(mass), G * N * 4) == 0
+    try:
+        desc = mcs.desc_for(q)
+        st = lib.mcs_anchor_select_topk(ctypes.byref(desc), ctypes.c_void_p(q.data_ptr()),
+                                        ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(lse.data_ptr()),
+                                        ctypes.c_void_p(perm.data_ptr()), T, K, ctypes.c_void_p(idx.data_ptr()),
+                                        mass, None, 0,
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0, lib.mcs_last_error()
+        torch.cuda.synchronize()
+    finally:
+        hip.hipFree(mass)
+    got = idx[0, 0].cpu().numpy()
+    want = expected(kcol, K)
+    for g in range(G):
+        assert np.array_equal(got[g], want), f"N={N} group {g}"
