@@ -365,90 +365,19 @@ def run_kernel_only(args, w):
 
 
 def run_variants(args, w):
-    """Selection variants on synthetic data, the ablation axes of the paper
-    landing page (Tables 3-4): query order (PDDP groups, whitened PDDP
-    groups, or consecutive tokens) x selection granularity (single keys vs
-    64-key blocks), at the
-    same realised density. Per variant: recall = mean over groups of the
-    selected keys' share of the group's exact probability mass; the sparse
-    output's relative L1 error against dense at the anchor (no R); and the
-    reuse output's error (sparse + R) against dense on the drifted steps.
-    Diagnostics only: the block variant picks its blocks with torch from the
-    library's exact group masses; the partial last block (N mod 64 keys) is
-    never a candidate, so every block variant keeps exactly K' keys."""
+    """Selection variants on synthetic data (paper landing page, Tables 3-4):
+    query order (PDDP groups, whitened PDDP groups, or consecutive tokens) x
+    granularity (single keys vs 64-key blocks) at a matched realised density;
+    recall, anchor and reuse errors per variant. The pipeline lives in the
+    package (variants.run); this prints its result as one JSON line."""
     import torch
 
     from sparse_attention_diffusion_pddp_amd import binding as mcs
-    from sparse_attention_diffusion_pddp_amd import synth
+    from sparse_attention_diffusion_pddp_amd import variants
 
     mcs.load()
     torch.cuda.set_device(0)
-    B, H, N, d, T, K, G = w.batch, w.heads, w.seqlen, w.head_dim, w.group_size, w.topk, w.groups
-    BLK = 64
-    nb = max(1, round(K / BLK))
-    Kb = nb * BLK
-    steps = [synth.make_qkv(w, seed=args.seed)]
-    for s_ in range(1, max(1, w.reuse_steps) + 1):
-        steps.append(synth.drift_qkv(w, steps[-1], step=s_, seed=args.seed))
-    dev = [tuple(t.cuda() for t in x) for x in steps]
-    q, k, v = dev[0]
-    desc = mcs.desc_for(q)
-    dense = []
-    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    for i, (qs, ks, vs) in enumerate(dev):
-        o = torch.empty_like(qs)
-        mcs.anchor_dense_lse(qs, ks, vs, o, lse if i == 0 else None)
-        dense.append(o)
-    lse0 = lse.clone()
-
-    def rel_l1(a, b):
-        return float((a.float() - b.float()).abs().sum() / b.float().abs().sum())
-
-    ws = torch.empty(mcs.pddp_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
-    perm_pddp = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
-    perm_white = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
-    grouping_ms = {}
-    for name, perm_, white in (("pddp", perm_pddp, False), ("pddp_whitened", perm_white, True)):
-        mcs.pddp_group(q, T, perm_, ws, whiten=white)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
-            mcs.pddp_group(q, T, perm_, ws, whiten=white)
-        e1.record()
-        torch.cuda.synchronize()
-        grouping_ms[name] = round(e0.elapsed_time(e1) / 5, 3)
-    perm_none = torch.arange(N, dtype=torch.int32, device="cuda").expand(B, H, N).contiguous()
-    sizes = torch.full((G,), float(T), device="cuda")
-    sizes[-1] = N - (G - 1) * T
-    mass = torch.empty((B, H, G, N), dtype=torch.float32, device="cuda")
-    out = torch.empty_like(q)
-    rows = []
-    for order, perm in (("pddp", perm_pddp), ("pddp_whitened", perm_white), ("none", perm_none)):
-        idx_tok = torch.empty((B, H, G, K), dtype=torch.int32, device="cuda")
-        mcs.anchor_select_topk(q, k, lse0, perm, T, K, idx_tok, group_mass=mass)
-        full = (N // BLK) * BLK
-        bmass = mass[..., :full].reshape(B, H, G, N // BLK, BLK).sum(-1)
-        top = torch.topk(bmass, nb, dim=-1).indices.sort(dim=-1).values
-        idx_blk = (top.unsqueeze(-1) * BLK + torch.arange(BLK, device="cuda")).reshape(B, H, G, Kb).to(torch.int32)
-        for gran, idx, kk in (("token", idx_tok, K), ("block64", idx_blk.contiguous(), Kb)):
-            recall = float((mass.gather(-1, idx.long()).sum(-1) / sizes).mean())
-            mcs.sparse_apply(q, k, v, perm, T, idx, kk, None, out)
-            err_anchor = rel_l1(out, dense[0])
-            r = torch.empty_like(q)
-            mcs.residual(q, k, v, dense[0], perm, T, idx, kk, r)
-            errs = []
-            for (qs, ks, vs), od in zip(dev[1:], dense[1:]):
-                mcs.sparse_apply(qs, ks, vs, perm, T, idx, kk, r, out)
-                errs.append(rel_l1(out, od))
-            rows.append({"order": order, "granularity": gran, "keys": kk,
-                         "density_pct": round(100.0 * kk / N, 2), "recall": round(recall, 4),
-                         "rel_l1_sparse_anchor": round(err_anchor, 4),
-                         "rel_l1_reuse_with_R": [round(e, 4) for e in errs]})
-    torch.cuda.synchronize()
-    print(json.dumps({"workload": w.name, "config": {"heads": H, "seqlen": N, "head_dim": d, "group_size": T,
-                                                     "density_pct": w.density_pct, "reuse_steps": len(dev) - 1,
-                                                     "drift": w.drift, "seed": args.seed},
-                      "grouping_ms": grouping_ms, "variants": rows}), flush=True)
+    print(json.dumps(variants.run(w, seed=args.seed)), flush=True)
 
 
 def main():
@@ -551,23 +480,26 @@ def main():
 
     stages = ["pddp", "dense_lse", "select_topk", "residual"] + [f"reuse{s}" for s in range(1, R_STEPS + 1)]
 
+    # cold caches: before every timed stage a 1 GiB write evicts the L2s and
+    # the 256 MB MALL, so each stage starts from HBM; the events bracket the
+    # stage alone
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
     def step(ev):
-        ev[0].record()
-        mcs.pddp_group(dq, T, perm, ws_pddp)
-        ev[1].record()
-        mcs.anchor_dense_lse(dq, dk, dv, o, lse)
-        ev[2].record()
-        mcs.anchor_select_topk(dq, dk, lse, perm, T, K, idx, ws=ws_sel)
-        ev[3].record()
-        mcs.residual(dq, dk, dv, o, perm, T, idx, K, r)
-        ev[4].record()
-        for s in range(1, R_STEPS + 1):
-            qt, kt, vt = dev[s]
-            mcs.sparse_apply(qt, kt, vt, perm, T, idx, K, r, ot[s - 1])
-            ev[4 + s].record()
+        calls = [lambda: mcs.pddp_group(dq, T, perm, ws_pddp),
+                 lambda: mcs.anchor_dense_lse(dq, dk, dv, o, lse),
+                 lambda: mcs.anchor_select_topk(dq, dk, lse, perm, T, K, idx, ws=ws_sel),
+                 lambda: mcs.residual(dq, dk, dv, o, perm, T, idx, K, r)]
+        calls += [(lambda s_: lambda: mcs.sparse_apply(*dev[s_], perm, T, idx, K, r, ot[s_ - 1]))(s)
+                  for s in range(1, R_STEPS + 1)]
+        for j, call in enumerate(calls):
+            flush.fill_(j)
+            ev[2 * j].record()
+            call()
+            ev[2 * j + 1].record()
 
     def new_events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+        return [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(stages))]
 
     for _ in range(args.warmup):
         step(new_events())
@@ -581,11 +513,25 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    stage_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, name in enumerate(stages)}
+    stage_ms = {name: sum(e[2 * j].elapsed_time(e[2 * j + 1]) for e in evs) / args.steps
+                for j, name in enumerate(stages)}
     anchor_ms = sum(stage_ms[s] for s in stages[:4])
     reuse_ms = sum(stage_ms[f"reuse{s}"] for s in range(1, R_STEPS + 1)) / R_STEPS
     flops = metrics.sparse_flops(B, H, N, K, d)
     value = flops / (reuse_ms * 1e-3) / 1e12
+
+    # warm caches (secondary): the reuse calls back to back, inputs left in L2/MALL
+    we = [torch.cuda.Event(enable_timing=True) for _ in range(2 * R_STEPS + 1)]
+    for s in range(1, R_STEPS + 1):
+        mcs.sparse_apply(*dev[s], perm, T, idx, K, r, ot[s - 1])
+    we[0].record()
+    for i in range(2 * R_STEPS):
+        s = 1 + i % R_STEPS
+        mcs.sparse_apply(*dev[s], perm, T, idx, K, r, ot[s - 1])
+        we[i + 1].record()
+    torch.cuda.synchronize()
+    reuse_warm_ms = we[0].elapsed_time(we[-1]) / (2 * R_STEPS)
+    pddp_bytes = metrics.pddp_algorithmic_bytes(B, H, N, d, T)
 
     # the same library's dense path (lse = NULL), the speedup denominator
     o2 = torch.empty_like(dq)
@@ -624,7 +570,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seqlen": N, "grid": list(w.grid), "head_dim": d,
                    "group_size": T, "density_pct": w.density_pct, "topk": K, "reuse_steps": R_STEPS,
-                   "seed": args.seed},
+                   "caches": "cold (1 GiB write before each timed stage)", "seed": args.seed},
+        "reuse_step_ms_warm": round(reuse_warm_ms, 4),
+        "value_warm": round(flops / (reuse_warm_ms * 1e-3) / 1e12, 2),
+        "pddp": {"ms": round(stage_ms["pddp"], 4), "algorithmic_bytes": pddp_bytes,
+                 "GBps": round(pddp_bytes / (stage_ms["pddp"] * 1e-3) / 1e9, 1),
+                 "frac_hbm": round(pddp_bytes / (stage_ms["pddp"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "anchor_step_ms": round(anchor_ms, 3),
         "anchor_stages_ms": {s: round(stage_ms[s], 3) for s in stages[:4]},
         "reuse_step_ms": round(reuse_ms, 4),

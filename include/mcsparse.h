@@ -168,6 +168,32 @@ mcs_status_t mcs_anchor_select_topk(const mcs_attn_desc_t *desc, const void *q, 
                                     size_t ws_bytes, mcs_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Step 2b at block granularity: the selection-granularity ablation of the
+ * paper landing page (Tables 3-4: single KV tokens against KV blocks at a
+ * matched density). A block is `block` consecutive keys; its mass is the sum
+ * of the exact group mass A[g][j] of its keys. Only the floor(N / block) full
+ * blocks are candidates (a short last block would keep fewer keys). The
+ * `nblocks` blocks of largest mass are chosen, equal mass -> lower block,
+ * and their keys written block by block, ascending:
+ *   kv_idx[b][h][g][i*block + t] = c_i*block + t, with c_0 < c_1 < ...
+ *   group_mass  fp32 [B][H][G][N] from mcs_anchor_select_topk.
+ *   block       a multiple of 64 in [64, 4096] (else MCS_ERR_UNSUPPORTED);
+ *               N must hold at least one full block.
+ *   nblocks     in [1, floor(N / block)].
+ *   kv_idx      out, int32 [B][H][G][nblocks * block]: a key list like
+ *               mcs_anchor_select_topk's, for mcs_residual / mcs_sparse_apply
+ *               with topk = nblocks * block.
+ *   ws          at least mcs_select_blocks_workspace_size() bytes (block
+ *               sums and chosen block ids), 16-byte aligned.
+ * kv_idx and ws must not overlap group_mass or each other.
+ * ------------------------------------------------------------------------ */
+mcs_status_t mcs_select_blocks_workspace_size(const mcs_attn_desc_t *desc, int32_t group_size, int32_t block,
+                                              int32_t nblocks, size_t *bytes);
+mcs_status_t mcs_select_blocks(const mcs_attn_desc_t *desc, const float *group_mass, int32_t group_size,
+                               int32_t block, int32_t nblocks, int32_t *kv_idx, void *ws, size_t ws_bytes,
+                               mcs_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Step 3: anchor residual (research walkthrough page, method step 3: run the
  * sparse attention once more at the same anchor; R = dense - sparse).
  *   O_sparse(i) = sum_{j in S_g} softmax_{S_g}(scale * q_i . k_j) v_j, with

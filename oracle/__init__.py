@@ -24,6 +24,9 @@ __all__ = [
     "sparse_attention",
     "residual",
     "reuse_output",
+    "block_select",
+    "group_recall",
+    "rel_l1",
     "reuse_head",
     "anchor_head",
 ]

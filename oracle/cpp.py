@@ -39,6 +39,9 @@ _SIGS = {
     "orc_sparse_attention": (None, [_pd, _i32, _pd, _pd, _i32, _pl, _i32, _d, _pd]),
     "orc_residual": (None, [_pd, _pd, _i64, _pd]),
     "orc_reuse_output": (None, [_pd, _i32, _pd, _pd, _i32, _pl, _i32, _pd, _d, _pd]),
+    "orc_block_select": (None, [_pd, _i32, _i32, _i32, _pl]),
+    "orc_group_recall": (_d, [_pd, _pl, _i32, _i32]),
+    "orc_rel_l1": (_d, [_pd, _pd, _i64]),
     "orc_reuse_head": (None, [_pd, _pd, _pd, _i32, _i32, _pl, _i32, _pl, _i64, _pl, _i32, _pd, _d, _i32, _pd]),
     "orc_anchor_head": (None, [_pd, _pd, _pd, _i32, _i32, _pl, _i32, _i32, _d, _i32, _pd, _pd, _pl, _pd, _pd]),
 }
@@ -159,6 +162,32 @@ class CppOracle:
         self.lib.orc_reuse_output(_p(q), q.shape[0], _p(k), _p(v), q.shape[1], _pi(idx), idx.shape[0], _p(r),
                                   float(scale), _p(o))
         return o
+
+    # ---- selection variants (granularity ablation) ----------------------------
+    def block_select(self, A, nblocks: int, block: int):
+        """Keys of the `nblocks` full `block`-key blocks of largest summed
+        mass (equal mass -> lower block), block by block, ascending."""
+        A = _f64(A)
+        N = A.shape[0]
+        if not 1 <= int(block) <= N or not 1 <= int(nblocks) <= N // int(block):
+            raise ValueError("need 1 <= block <= N and 1 <= nblocks <= N // block")
+        idx = np.empty(int(nblocks) * int(block), dtype=np.int64)
+        self.lib.orc_block_select(_p(A), N, int(block), int(nblocks), _pi(idx))
+        return idx
+
+    def group_recall(self, A, idx, n_rows: int) -> float:
+        """Mean over the group's rows of the probability mass of the selected keys."""
+        A, idx = _f64(A), _i64a(idx)
+        if idx.size and (idx.min() < 0 or idx.max() >= A.shape[0]):
+            raise ValueError("key index out of range")
+        return float(self.lib.orc_group_recall(_p(A), _pi(idx), idx.shape[0], int(n_rows)))
+
+    def rel_l1(self, x, ref) -> float:
+        """sum |x - ref| / sum |ref|."""
+        x, ref = _f64(x), _f64(ref)
+        if x.shape != ref.shape:
+            raise ValueError("x and ref must have one shape")
+        return float(self.lib.orc_rel_l1(_p(x), _p(ref), x.size))
 
     # ---- whole-head drivers (std::thread over the head's groups) -------------
     def reuse_head(self, q, k, v, perm, group_size: int, idx, r, scale: float, groups=None):

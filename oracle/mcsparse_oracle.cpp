@@ -467,6 +467,48 @@ void orc_reuse_output(const double *q_rows, int32_t M, const double *k, const do
   for (int64_t e = 0; e < (int64_t)M * d; ++e) o[e] = round_bf16_one(o[e] + r[e]);
 }
 
+// Block granularity (paper landing page, Tables 3-4, the granularity
+// ablation): block b holds keys [b*block, (b+1)*block); its mass is the sum
+// of its keys' group mass, in key order. Only the floor(N/block) full blocks
+// compete; the `nblocks` of largest mass win, equal mass -> lower block. The
+// winners' keys are written block by block, ascending.
+void orc_block_select(const double *A, int32_t N, int32_t block, int32_t nblocks, int64_t *idx) {
+#if ORC_MUTANT == 13
+  const int64_t nfull = (N + block - 1) / block;  // planted: the short last block competes
+#else
+  const int64_t nfull = N / block;
+#endif
+  std::vector<double> bm(nfull, 0.0);
+  for (int64_t b = 0; b < nfull; ++b)
+    for (int64_t t = 0; t < block && b * block + t < N; ++t) bm[b] += A[b * block + t];
+  std::vector<int64_t> sel(nblocks);
+  topk_select(bm.data(), (int)nfull, nblocks, sel.data());
+  for (int64_t i = 0; i < nblocks; ++i)
+    for (int64_t t = 0; t < block; ++t) idx[i * block + t] = std::min<int64_t>(sel[i] * block + t, N - 1);
+}
+
+// Recall of a selection: the mean over the group's n_rows query rows of the
+// probability mass its selected keys carry, (1/n_rows) sum_{j in idx} A_j.
+double orc_group_recall(const double *A, const int64_t *idx, int32_t K, int32_t n_rows) {
+  double s = 0.0;
+  for (int32_t t = 0; t < K; ++t) s += A[idx[t]];
+#if ORC_MUTANT == 14
+  return s / K;  // planted: divided by the key count
+#else
+  return s / n_rows;
+#endif
+}
+
+// Relative L1 error: sum |x - ref| / sum |ref|.
+double orc_rel_l1(const double *x, const double *ref, int64_t n) {
+  double num = 0.0, den = 0.0;
+  for (int64_t e = 0; e < n; ++e) {
+    num += std::fabs(x[e] - ref[e]);
+    den += std::fabs(ref[e]);
+  }
+  return num / den;
+}
+
 // A head's reuse step over groups: entry e of `gids` (or e itself when gids
 // is NULL) names group g, whose rows are perm[g*T : min((g+1)*T, N)] and
 // whose indices are idx[e]; each entry on its own worker. q, k, v, r and out

@@ -68,6 +68,9 @@ __all__ = [
     "sparse_attention",
     "residual",
     "reuse_output",
+    "block_select",
+    "group_recall",
+    "rel_l1",
 ]
 
 
@@ -261,3 +264,28 @@ def residual(o_dense_stored: np.ndarray, o_sparse: np.ndarray) -> np.ndarray:
 def reuse_output(q_rows, k, v, idx, r_stored, scale) -> np.ndarray:
     """Reuse step: bf16(SparseAttn(fresh Q, K, V; cached idx) + cached R)."""
     return round_bf16(sparse_attention(q_rows, k, v, idx, scale) + r_stored)
+
+
+# ---------------------------------------------------------------------------
+# selection variants: block granularity, recall, output error
+# ---------------------------------------------------------------------------
+
+def block_select(A: np.ndarray, nblocks: int, block: int) -> np.ndarray:
+    """Block granularity: block b is keys [b*block, (b+1)*block) and its mass
+    the sum of theirs; among the N // block full blocks the ``nblocks`` of
+    largest mass win (equal mass -> lower block); their keys, ascending."""
+    nfull = A.shape[0] // block
+    bm = A[: nfull * block].reshape(nfull, block).sum(axis=1)
+    b = np.arange(nfull)
+    chosen = np.sort(np.lexsort((b, -bm))[:nblocks])
+    return (chosen[:, None] * block + np.arange(block)[None, :]).reshape(-1).astype(np.int64)
+
+
+def group_recall(A: np.ndarray, idx: np.ndarray, n_rows: int) -> float:
+    """Mean over the group's rows of the probability mass its selected keys carry."""
+    return float(A[idx].sum() / n_rows)
+
+
+def rel_l1(x: np.ndarray, ref: np.ndarray) -> float:
+    """sum |x - ref| / sum |ref|."""
+    return float(np.abs(x - ref).sum() / np.abs(ref).sum())

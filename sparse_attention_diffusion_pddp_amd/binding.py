@@ -33,6 +33,8 @@ SIGNATURES = [
     ("mcs_anchor_dense_lse", _i32, [_p, _p, _p, _p, _p, _p, _p]),
     ("mcs_anchor_select_topk_workspace_size", _i32, [_p, _i32, _i32, ctypes.POINTER(_sz)]),
     ("mcs_anchor_select_topk", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _sz, _p]),
+    ("mcs_select_blocks_workspace_size", _i32, [_p, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    ("mcs_select_blocks", _i32, [_p, _p, _i32, _i32, _i32, _p, _p, _sz, _p]),
     ("mcs_residual", _i32, [_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p]),
     ("mcs_sparse_apply", _i32, [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p]),
     ("mcs_kv_idx_bitmap_bytes", _i32, [_p, _i32, ctypes.POINTER(_sz)]),
@@ -206,6 +208,32 @@ def anchor_select_topk(q, k, lse, perm, group_size, topk, kv_idx, group_mass=Non
     _check("mcs_anchor_select_topk",
            lib.mcs_anchor_select_topk(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(lse), _ptr(perm), group_size, topk,
                                       _ptr(kv_idx), _ptr(group_mass), _ptr(ws), wsb, _stream(stream)))
+
+
+def select_blocks_workspace_size(desc: Desc, group_size: int, block: int, nblocks: int) -> int:
+    lib = load()
+    n = ctypes.c_size_t()
+    _check("mcs_select_blocks_workspace_size",
+           lib.mcs_select_blocks_workspace_size(ctypes.byref(desc), group_size, block, nblocks, ctypes.byref(n)))
+    return n.value
+
+
+def select_blocks(desc: Desc, group_mass, group_size, block, nblocks, kv_idx, ws=None, stream=None):
+    """mcs_select_blocks: the `nblocks` full blocks of `block` keys with the
+    largest summed group mass, expanded to ascending key indices
+    [B][H][G][nblocks * block]. Allocates the workspace when none is given."""
+    lib = load()
+    G = _groups(desc, group_size)
+    rows = desc.batch * desc.heads * G
+    _dev(group_mass, "group_mass", torch.float32, rows * desc.seqlen, contiguous=True)
+    _dev(kv_idx, "kv_idx", torch.int32, rows * nblocks * block, contiguous=True)
+    if ws is None:
+        ws = torch.empty(select_blocks_workspace_size(desc, group_size, block, nblocks), dtype=torch.uint8,
+                         device=group_mass.device)
+    _dev(ws, "ws", contiguous=True)
+    _check("mcs_select_blocks", lib.mcs_select_blocks(ctypes.byref(desc), _ptr(group_mass), group_size, block,
+                                                      nblocks, _ptr(kv_idx), _ptr(ws),
+                                                      ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def residual(q, k, v, o_dense, perm, group_size, kv_idx, topk, r, desc=None, stream=None):

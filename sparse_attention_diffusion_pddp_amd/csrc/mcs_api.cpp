@@ -295,6 +295,48 @@ mcs_status_t mcs_anchor_select_topk(const mcs_attn_desc_t *desc, const void *q, 
   return hip_status(mcs::launch_select(desc->head_dim, a, (hipStream_t)stream), "mcs_anchor_select_topk");
 }
 
+namespace {
+mcs_status_t check_block_args(const mcs_attn_desc_t *desc, int32_t group_size, int32_t block, int32_t nblocks) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_group(group_size));
+  if (block < 64 || block > 4096 || block % 64)
+    return fail(MCS_ERR_UNSUPPORTED, "block %d not supported (a multiple of 64 in [64, 4096])", block);
+  const int32_t nfull = desc->seqlen / block;
+  if (nfull < 1) return fail(MCS_ERR_INVALID_ARGUMENT, "seqlen %d holds no full block of %d keys", desc->seqlen, block);
+  if (nblocks < 1 || nblocks > nfull)
+    return fail(MCS_ERR_INVALID_ARGUMENT, "nblocks %d outside [1, %d] (full blocks)", nblocks, nfull);
+  return ok();
+}
+}  // namespace
+
+mcs_status_t mcs_select_blocks_workspace_size(const mcs_attn_desc_t *desc, int32_t group_size, int32_t block,
+                                              int32_t nblocks, size_t *bytes) {
+  MCS_TRY(check_block_args(desc, group_size, block, nblocks));
+  if (!bytes) return fail(MCS_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  const int64_t rows = (int64_t)desc->batch * desc->heads * groups_of(desc, group_size);
+  *bytes = mcs::select_blocks_ws_bytes(rows, desc->seqlen, block, nblocks);
+  return ok();
+}
+
+mcs_status_t mcs_select_blocks(const mcs_attn_desc_t *desc, const float *group_mass, int32_t group_size,
+                               int32_t block, int32_t nblocks, int32_t *kv_idx, void *ws, size_t ws_bytes,
+                               mcs_stream_t stream) {
+  MCS_TRY(check_block_args(desc, group_size, block, nblocks));
+  MCS_TRY(check_ptr(group_mass, "group_mass"));
+  MCS_TRY(check_ptr(kv_idx, "kv_idx"));
+  const int64_t rows = (int64_t)desc->batch * desc->heads * groups_of(desc, group_size);
+  const size_t need = mcs::select_blocks_ws_bytes(rows, desc->seqlen, block, nblocks);
+  if (ws_bytes < need) return fail(MCS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!ws || !aligned16(ws)) return fail(MCS_ERR_INVALID_ARGUMENT, "ws is NULL or not 16-byte aligned");
+  const int64_t mb = per_group_bytes(desc, group_size, desc->seqlen);
+  const int64_t ib = per_group_bytes(desc, group_size, (int64_t)nblocks * block);
+  MCS_TRY(check_disjoint({kv_idx, ib, "kv_idx"}, {{group_mass, mb, "group_mass"}, {ws, (int64_t)need, "ws"}}));
+  MCS_TRY(check_disjoint({ws, (int64_t)need, "ws"}, {{group_mass, mb, "group_mass"}}));
+  return hip_status(mcs::launch_select_blocks(group_mass, rows, desc->seqlen, block, nblocks, kv_idx, ws,
+                                              (hipStream_t)stream),
+                    "mcs_select_blocks");
+}
+
 mcs_status_t mcs_residual(const mcs_attn_desc_t *desc, const void *q, const void *k, const void *v,
                           const void *o_dense, const int32_t *perm, int32_t group_size,
                           const int32_t *kv_idx, int32_t topk, void *r, mcs_stream_t stream) {

@@ -39,6 +39,13 @@ struct SelectArgs {
 };
 hipError_t launch_select(int head_dim, const SelectArgs &a, hipStream_t s);
 
+// block-granularity selection over mass rows: block sums, top-nb blocks,
+// expansion to ascending key indices; ws holds the sums and the block ids
+size_t select_blocks_bsum_bytes(int64_t rows, int N, int blk);
+size_t select_blocks_ws_bytes(int64_t rows, int N, int blk, int nb);
+hipError_t launch_select_blocks(const float *mass, int64_t rows, int N, int blk, int nb, int32_t *kv_idx, void *ws,
+                                hipStream_t s);
+
 // bitmap form of the KV indices: ceil(N/32) words per (b, h, g) row
 size_t idx_bitmap_words(int N);
 hipError_t launch_idx_encode(const int32_t *idx, int64_t rows, int K, int N, uint32_t *bitmap, hipStream_t s);

@@ -462,6 +462,20 @@ static hipError_t launch_mass(const SelectArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// top-K of every row of a.mass (a.B * a.H * a.G rows of a.N keys) into a.idx
+static hipError_t launch_topk(const SelectArgs &a, hipStream_t s) {
+  const dim3 grid(a.B * a.H * a.G);
+  if (a.N <= 512 * 8) hipLaunchKernelGGL((topk_reg_kernel<512, 8>), grid, dim3(512), 0, s, a);
+  else if (a.N <= 512 * 16) hipLaunchKernelGGL((topk_reg_kernel<512, 16>), grid, dim3(512), 0, s, a);
+  else if (a.N <= 512 * 32) hipLaunchKernelGGL((topk_reg_kernel<512, 32>), grid, dim3(512), 0, s, a);
+  else if (a.N <= 512 * 64) hipLaunchKernelGGL((topk_reg_kernel<512, 64>), grid, dim3(512), 0, s, a);
+  else if (a.N <= 512 * 128) hipLaunchKernelGGL((topk_reg_kernel<512, 128>), grid, dim3(512), 0, s, a);
+  // 12 waves, three per SIMD: up to 168 VGPRs, room for 128 keys a lane
+  else if (a.N <= 768 * 128) hipLaunchKernelGGL((topk_reg_kernel<768, 128>), grid, dim3(768), 0, s, a);
+  else hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(int head_dim, const SelectArgs &a, hipStream_t s) {
   const int nblocks = a.B * a.H * a.G;
   if (nblocks <= 0) return hipSuccess;
@@ -472,16 +486,72 @@ hipError_t launch_select(int head_dim, const SelectArgs &a, hipStream_t s) {
   else if (head_dim == 64 && a.T == 64) e = launch_mass<64, 2>(a, s);
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
-  const dim3 grid(nblocks);
-  if (a.N <= 512 * 8) hipLaunchKernelGGL((topk_reg_kernel<512, 8>), grid, dim3(512), 0, s, a);
-  else if (a.N <= 512 * 16) hipLaunchKernelGGL((topk_reg_kernel<512, 16>), grid, dim3(512), 0, s, a);
-  else if (a.N <= 512 * 32) hipLaunchKernelGGL((topk_reg_kernel<512, 32>), grid, dim3(512), 0, s, a);
-  else if (a.N <= 512 * 64) hipLaunchKernelGGL((topk_reg_kernel<512, 64>), grid, dim3(512), 0, s, a);
-  else if (a.N <= 512 * 128) hipLaunchKernelGGL((topk_reg_kernel<512, 128>), grid, dim3(512), 0, s, a);
-  // 12 waves, three per SIMD: up to 168 VGPRs, room for 128 keys a lane
-  else if (a.N <= 768 * 128) hipLaunchKernelGGL((topk_reg_kernel<768, 128>), grid, dim3(768), 0, s, a);
-  else hipLaunchKernelGGL(topk_kernel, grid, dim3(kTopkThreads), 0, s, a);
+  return launch_topk(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// Block-granularity selection (the granularity ablation of the paper landing
+// page, Tables 3-4): a block is `blk` consecutive keys; its mass is the sum
+// of its keys' exact group mass. Only the N / blk full blocks are candidates.
+// ---------------------------------------------------------------------------
+
+// One workgroup per mass row, each wave one block at a time: lane l adds the
+// block's keys l, l + 64, ... in order, then a fixed butterfly over the wave.
+__global__ __launch_bounds__(256) void block_sum_kernel(const float *mass, int N, int blk, int nfull,
+                                                        float *bsum) {
+  const int64_t row = blockIdx.x;
+  const float *A = mass + row * N;
+  float *out = bsum + row * nfull;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int b = wave; b < nfull; b += 4) {
+    float x = 0.f;
+    for (int j = lane; j < blk; j += 64) x += A[(int64_t)b * blk + j];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    if (lane == 0) out[b] = x;
+  }
+}
+
+// kv_idx row = the chosen blocks' keys, block by block (blocks ascending)
+__global__ __launch_bounds__(256) void block_expand_kernel(const int32_t *bidx, int nb, int blk, int32_t *kv_idx) {
+  const int64_t row = blockIdx.y;
+  const int K = nb * blk;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= K) return;
+  kv_idx[row * K + i] = bidx[row * nb + i / blk] * blk + i % blk;
+}
+
+hipError_t launch_select_blocks(const float *mass, int64_t rows, int N, int blk, int nb, int32_t *kv_idx, void *ws,
+                                hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int nfull = N / blk;
+  float *bsum = (float *)ws;
+  int32_t *bidx = (int32_t *)((char *)ws + select_blocks_bsum_bytes(rows, N, blk));
+  hipLaunchKernelGGL(block_sum_kernel, dim3((unsigned)rows), dim3(256), 0, s, mass, N, blk, nfull, bsum);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SelectArgs a{};
+  a.mass = bsum;
+  a.idx = bidx;
+  a.B = 1;
+  a.H = 1;
+  a.G = (int32_t)rows;
+  a.N = nfull;
+  a.K = nb;
+  e = launch_topk(a, s);
+  if (e != hipSuccess) return e;
+  const int K = nb * blk;
+  hipLaunchKernelGGL(block_expand_kernel, dim3((unsigned)((K + 255) / 256), (unsigned)rows), dim3(256), 0, s, bidx,
+                     nb, blk, kv_idx);
   return hipGetLastError();
+}
+
+size_t select_blocks_bsum_bytes(int64_t rows, int N, int blk) {
+  return ((size_t)rows * (size_t)(N / blk) * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t select_blocks_ws_bytes(int64_t rows, int N, int blk, int nb) {
+  return select_blocks_bsum_bytes(rows, N, blk) + (size_t)rows * nb * sizeof(int32_t);
 }
 
 }  // namespace mcs

@@ -23,6 +23,22 @@ def select_sweep_flops(batch, heads, seqlen, head_dim) -> int:
     return 2 * batch * heads * seqlen * seqlen * head_dim
 
 
+def pddp_levels(seqlen: int, group_size: int) -> int:
+    """Depth of the PDDP tree: splits until every node holds at most one tile."""
+    levels, n = 0, seqlen
+    while n > group_size:  # the right child, never smaller than the left, is the deepest
+        G = -(-n // group_size)
+        n = n - (G // 2) * group_size
+        levels += 1
+    return levels
+
+
+def pddp_algorithmic_bytes(batch, heads, seqlen, head_dim, group_size, elem_bytes=2) -> int:
+    """Bytes the grouping must move at the least: one read of every query per
+    tree level, plus the int32 group order written once."""
+    return batch * heads * (pddp_levels(seqlen, group_size) * seqlen * head_dim * elem_bytes + seqlen * 4)
+
+
 def kernel_speedup(t_dense, t_sparse, density):
     """Attention-kernel speedup rho = t_dense / t_sparse and efficiency eta = rho * s
     against the ideal 1/s speedup (paper landing page, Table 6)."""
@@ -60,3 +76,27 @@ def anchor_overhead_points(t_anchor_only_ms, t_dense_ms, anchors=2, steps=40):
     """Anchor-only work expressed as extra attention density, in percentage
     points, for ``anchors`` anchors over ``steps`` sparse steps."""
     return 100.0 * (anchors / steps) * t_anchor_only_ms / t_dense_ms
+
+
+def matched_blocks(topk: int, block: int) -> int:
+    """Blocks of `block` keys that match a density of `topk` single keys:
+    the nearest whole number of blocks (halves up), at least one."""
+    return max(1, (topk + block // 2) // block)
+
+
+def group_recall(mass, kv_idx, group_rows):
+    """Per group, the mean over its query rows of the probability mass of the
+    selected keys: sum_{j in S_g} A[g][j] / |g|. mass [..., G, N] and kv_idx
+    [..., G, K] are torch tensors; group_rows [G] the rows of each group."""
+    import torch
+
+    sel = mass.gather(-1, kv_idx.long()).to(torch.float64).sum(-1)
+    return sel / group_rows.to(torch.float64)
+
+
+def rel_l1(x, ref) -> float:
+    """sum |x - ref| / sum |ref| over two torch tensors of one shape."""
+    import torch
+
+    x64, r64 = x.to(torch.float64), ref.to(torch.float64)
+    return float((x64 - r64).abs().sum() / r64.abs().sum())

@@ -5,7 +5,7 @@ numpy oracle: each case swaps one function for a copy with a plausible slip
 wrong tie rule) and runs the pin that should catch it.
 
 C++ oracle: the same kinds of slip are compiled into copies of the library
-(ORC_MUTANT = 1..12 in mcsparse_oracle.cpp, one slip each), and each copy
+(ORC_MUTANT = 1..14 in mcsparse_oracle.cpp, one slip each), and each copy
 must fail its pin. Everything runs on the CPU and touches only the oracle.
 """
 import math
@@ -99,6 +99,19 @@ def _std_times_sd(q):
     return Xc * np.sqrt(var), var  # inverted scale
 
 
+def _blocks_with_partial(A, nblocks, block):
+    N = A.shape[0]
+    nb_all = -(-N // block)
+    pad = np.concatenate([A, np.zeros(nb_all * block - N)])
+    bm = pad.reshape(nb_all, block).sum(axis=1)  # the short last block competes
+    chosen = np.sort(np.lexsort((np.arange(nb_all), -bm))[:nblocks])
+    return np.minimum((chosen[:, None] * block + np.arange(block)).reshape(-1), N - 1)
+
+
+def _recall_over_keys(A, idx, n_rows):
+    return float(A[idx].sum() / len(idx))
+
+
 MUTANTS = [
     ("dense_lse", _dense_no_scale, pins.test_dense_lse_matches_torch_sdpa_and_scipy_logsumexp),
     ("dense_lse", _dense_transposed, pins.test_dense_lse_decimal_bruteforce),
@@ -113,6 +126,8 @@ MUTANTS = [
     ("standardize", _std_unscaled, pins.test_whitened_pddp_root_split_follows_the_correlation_eigenvector),
     ("standardize", _std_by_variance, pins.test_whitened_pddp_root_split_follows_the_correlation_eigenvector),
     ("standardize", _std_times_sd, pins.test_standardize_closed_form_and_constant_dims),
+    ("block_select", _blocks_with_partial, pins.test_block_select_bruteforce_ties_and_partial_block),
+    ("group_recall", _recall_over_keys, pins.test_group_recall_closed_forms),
 ]
 
 
@@ -145,6 +160,8 @@ CPP_MUTANTS = {
     10: pins.test_whitened_pddp_root_split_follows_the_correlation_eigenvector,  # never scaled
     11: pins.test_residual_closed_form_and_anchor_identity,          # sparse - dense
     12: pins.test_round_bf16_matches_torch_rne,                      # truncation
+    13: pins.test_block_select_bruteforce_ties_and_partial_block,    # the short last block competes
+    14: pins.test_group_recall_closed_forms,                         # divided by the key count
 }
 
 

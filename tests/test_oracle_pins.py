@@ -465,3 +465,56 @@ def test_topk_count_integer_ceil(O):
     assert O.topk_count(15, 64000) == 9600
     assert O.topk_count(100, 77) == 77
     assert O.topk_count(1, 1) == 1
+
+
+# ---------------------------------------------------------------------------
+# selection variants (block granularity, recall, output error)
+# ---------------------------------------------------------------------------
+
+def test_block_select_of_one_key_blocks_is_the_token_topk(O):
+    rng = np.random.default_rng(30)
+    A = rng.integers(0, 9, 500).astype(float) / 7.0  # many ties
+    for K in (1, 37, 250, 500):
+        assert O.block_select(A, K, 1).tolist() == O.topk_select(A, K).tolist()
+
+
+def test_block_select_bruteforce_ties_and_partial_block(O):
+    rng = np.random.default_rng(31)
+    N, blk = 1000, 64  # 15 full blocks, keys 960..999 a partial block
+    A = rng.random(N)
+    A[960:] = 1e6  # the partial block never competes
+    A[64:128] = A[192:256]  # blocks 1 and 3 tie exactly: the lower one ranks first
+    sums = [math.fsum(A[b * blk:(b + 1) * blk]) for b in range(N // blk)]
+    for nb in (1, 4, 9, 15):
+        order = sorted(range(N // blk), key=lambda b: (-sums[b], b))[:nb]
+        want = [b * blk + t for b in sorted(order) for t in range(blk)]
+        assert O.block_select(A, nb, blk).tolist() == want
+    # with the tie at the cut, exactly one of blocks 1 and 3 is kept: block 1
+    rank = sorted(range(N // blk), key=lambda b: (-sums[b], b))
+    cut = rank.index(1) + 1
+    got = set(O.block_select(A, cut, blk).tolist())
+    assert set(range(64, 128)) <= got and not set(range(192, 256)) & got
+
+
+def test_group_recall_closed_forms(O):
+    rng = np.random.default_rng(32)
+    q, k = bf16_values(rng, (12, 8)), bf16_values(rng, (90, 8))
+    _, L = O.dense_lse(q, k, np.zeros((90, 8)), 0.6)
+    A = O.group_mass(q, k, L, 0.6)
+    # every key: each row's probabilities sum to 1
+    assert abs(O.group_recall(A, np.arange(90), 12) - 1.0) < 1e-13
+    # a hand sum
+    idx = np.array([3, 17, 40])
+    assert O.group_recall(A, idx, 12) == pytest.approx(float(sum(A[[3, 17, 40]])) / 12, rel=1e-15, abs=0)
+    # the top-K carry at least as much mass as any other K keys
+    top = O.topk_select(A, 20)
+    for _ in range(20):
+        other = np.sort(rng.choice(90, 20, replace=False))
+        assert O.group_recall(A, top, 12) >= O.group_recall(A, other, 12)
+
+
+def test_rel_l1_closed_form(O):
+    assert O.rel_l1(np.array([1.0, 2.0, 3.0]), np.array([1.0, 1.0, -1.0])) == pytest.approx((0 + 1 + 4) / 3)
+    x = np.arange(12.0).reshape(3, 4) - 5
+    assert O.rel_l1(x, x) == 0.0
+    assert O.rel_l1(2 * x, x) == pytest.approx(1.0)

@@ -52,3 +52,25 @@ def test_work_counts():
     assert metrics.dense_flops(1, 40, 75600, 128) == 117_050_572_800_000
     assert abs(metrics.align_ratio(32760, 128, 4914, 64) - 1.0032) < 1e-3
     assert metrics.align_ratio(1024, 64, 256, 64) == 1.0
+
+
+def test_recall_and_rel_l1_formulas_match_the_oracle():
+    """metrics.group_recall / rel_l1 (torch reductions used by the variant
+    diagnostics) against the oracle's definitions, on the CPU."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from sparse_attention_diffusion_pddp_amd import metrics
+    rng = np.random.default_rng(40)
+    A = rng.random((3, 7, 300))
+    idx = np.sort(np.stack([np.stack([rng.choice(300, 45, replace=False) for _ in range(7)]) for _ in range(3)]), -1)
+    rows = torch.tensor([128.0] * 6 + [44.0])
+    got = metrics.group_recall(torch.from_numpy(A), torch.from_numpy(idx), rows).numpy()
+    for h in range(3):
+        for g in range(7):
+            assert abs(got[h, g] - O.group_recall(A[h, g], idx[h, g], int(rows[g]))) < 1e-14
+    x, ref = rng.standard_normal((50, 9)), rng.standard_normal((50, 9))
+    assert abs(metrics.rel_l1(torch.from_numpy(x), torch.from_numpy(ref)) - O.rel_l1(x, ref)) < 1e-14
+    assert metrics.matched_blocks(4914, 64) == 77 and metrics.matched_blocks(8190, 64) == 128
+    assert metrics.matched_blocks(10, 64) == 1 and metrics.matched_blocks(96, 64) == 2
