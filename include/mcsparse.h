@@ -132,6 +132,25 @@ mcs_status_t mcs_pddp_group_ex(const mcs_attn_desc_t *desc, const void *q, int32
                                int32_t power_iters, uint32_t flags, int32_t *perm, void *ws,
                                size_t ws_bytes, mcs_stream_t stream);
 
+/* Step 1 without any allocation, for callers that cannot call hipMalloc
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * it): the same grouping as mcs_pddp_group_ex, bitwise, with the workspace
+ * taken from a device array the library owns (MCS_PDDP_SCRATCH_BYTES =
+ * 64 MiB on each GPU it runs on, held until the process ends).
+ *   The heads are grouped in chunks whose workspace fits the scratch (they
+ *   are independent), one chunk after another on `stream`.
+ *   MCS_ERR_UNSUPPORTED: one head's workspace (mcs_pddp_group_workspace_size
+ *   with batch = heads = 1) exceeds the scratch; every workload shape here
+ *   fits (N = 98,304 at d = 128 needs about 59 MiB).
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *   on one GPU (other streams, other host threads) race and must be ordered
+ *   by the caller (one stream, or events). Nothing in the scratch needs to
+ *   start at zero. Other arguments and errors as mcs_pddp_group_ex. */
+#define MCS_PDDP_SCRATCH_BYTES ((size_t)64 << 20)
+mcs_status_t mcs_pddp_group_noalloc(const mcs_attn_desc_t *desc, const void *q, int32_t group_size,
+                                    int32_t power_iters, uint32_t flags, int32_t *perm,
+                                    mcs_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Step 2a: anchor dense attention with per-row log-sum-exp (research
  * walkthrough page, method step 2: dense attention and each row's LSE first).

@@ -30,6 +30,7 @@ SIGNATURES = [
     ("mcs_pddp_group_workspace_size", _i32, [_p, _i32, ctypes.POINTER(_sz)]),
     ("mcs_pddp_group", _i32, [_p, _p, _i32, _i32, _p, _p, _sz, _p]),
     ("mcs_pddp_group_ex", _i32, [_p, _p, _i32, _i32, ctypes.c_uint32, _p, _p, _sz, _p]),
+    ("mcs_pddp_group_noalloc", _i32, [_p, _p, _i32, _i32, ctypes.c_uint32, _p, _p]),
     ("mcs_anchor_dense_lse", _i32, [_p, _p, _p, _p, _p, _p, _p]),
     ("mcs_anchor_select_topk_workspace_size", _i32, [_p, _i32, _i32, ctypes.POINTER(_sz)]),
     ("mcs_anchor_select_topk", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _p, _p, _p, _sz, _p]),
@@ -181,6 +182,18 @@ def pddp_group(q, group_size, perm, ws, power_iters=16, desc=None, stream=None, 
         return
     _check("mcs_pddp_group", lib.mcs_pddp_group(ctypes.byref(desc), _ptr(q), group_size, power_iters, _ptr(perm),
                                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def pddp_group_noalloc(q, group_size, perm, power_iters=16, desc=None, stream=None, whiten=False):
+    """mcs_pddp_group_noalloc: the grouping with the library's own device
+    scratch, no workspace argument and no allocation."""
+    lib = load()
+    desc = desc or desc_for(q)
+    _tensors(("q", q))
+    _dev(perm, "perm", torch.int32, _per_token(desc), contiguous=True)
+    _check("mcs_pddp_group_noalloc",
+           lib.mcs_pddp_group_noalloc(ctypes.byref(desc), _ptr(q), group_size, power_iters,
+                                      PDDP_WHITEN if whiten else 0, _ptr(perm), _stream(stream)))
 
 
 def anchor_dense_lse(q, k, v, o, lse=None, desc=None, stream=None):

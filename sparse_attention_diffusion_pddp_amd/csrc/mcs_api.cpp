@@ -208,6 +208,43 @@ mcs_status_t mcs_pddp_group_ex(const mcs_attn_desc_t *desc, const void *q, int32
                     "mcs_pddp_group");
 }
 
+mcs_status_t mcs_pddp_group_noalloc(const mcs_attn_desc_t *desc, const void *q, int32_t group_size,
+                                    int32_t power_iters, uint32_t flags, int32_t *perm, mcs_stream_t stream) {
+  MCS_TRY(check_desc(desc));
+  MCS_TRY(check_group(group_size));
+  MCS_TRY(check_tensor(q, "q"));
+  MCS_TRY(check_ptr(perm, "perm"));
+  if (power_iters < 1 || power_iters > 64)
+    return fail(MCS_ERR_INVALID_ARGUMENT, "power_iters %d outside [1, 64]", power_iters);
+  if (flags & ~MCS_PDDP_WHITEN) return fail(MCS_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", flags);
+  const int N = desc->seqlen, D = desc->head_dim, H = desc->heads;
+  // heads are independent: run them in chunks whose workspace fits the
+  // library's scratch (the plan tables are shared by a chunk's heads)
+  const size_t one = mcs::pddp_workspace_bytes(1, 1, N, D, group_size);
+  if (one > mcs::kScratchBytes)
+    return fail(MCS_ERR_UNSUPPORTED, "one head needs %zu bytes of PDDP scratch, above the library's %zu",
+                one, mcs::kScratchBytes);
+  const size_t per_head = mcs::pddp_workspace_bytes(1, 2, N, D, group_size) - one;
+  int chunk = per_head == 0 ? H : (int)std::min<size_t>((size_t)H, 1 + (mcs::kScratchBytes - one) / per_head);
+  while (chunk > 1 && mcs::pddp_workspace_bytes(1, chunk, N, D, group_size) > mcs::kScratchBytes) --chunk;
+  MCS_TRY(check_disjoint({perm, per_token_bytes(desc), "perm"}, {{q, tensor_bytes(desc), "q"}}));
+  void *ws = nullptr;
+  const hipError_t e = mcs::scratch_address(&ws);
+  if (e != hipSuccess) return hip_status(e, "mcs_pddp_group_noalloc (scratch address)");
+  const uint16_t *qb = (const uint16_t *)q;
+  for (int b = 0; b < desc->batch; ++b)
+    for (int h0 = 0; h0 < H; h0 += chunk) {
+      const int nh = std::min(chunk, H - h0);
+      const uint16_t *qc = qb + (int64_t)b * desc->stride_b + (int64_t)h0 * desc->stride_h;
+      int32_t *pc = perm + ((int64_t)b * H + h0) * N;
+      const hipError_t le = mcs::run_pddp(qc, desc->stride_b, desc->stride_n, desc->stride_h, 1, nh, N, D,
+                                          group_size, power_iters, (flags & MCS_PDDP_WHITEN) != 0, pc, ws,
+                                          mcs::kScratchBytes, (hipStream_t)stream);
+      if (le != hipSuccess) return hip_status(le, "mcs_pddp_group_noalloc");
+    }
+  return ok();
+}
+
 mcs_status_t mcs_pddp_group(const mcs_attn_desc_t *desc, const void *q, int32_t group_size,
                             int32_t power_iters, int32_t *perm, void *ws, size_t ws_bytes,
                             mcs_stream_t stream) {

@@ -51,6 +51,11 @@ size_t idx_bitmap_words(int N);
 hipError_t launch_idx_encode(const int32_t *idx, int64_t rows, int K, int N, uint32_t *bitmap, hipStream_t s);
 hipError_t launch_idx_decode(const uint32_t *bitmap, int64_t rows, int K, int N, int32_t *idx, hipStream_t s);
 
+// Device scratch owned by the library (mcs_scratch.hip): kScratchBytes on
+// each GPU, whose address scratch_address() returns for the current device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_address(void **out);
+
 size_t pddp_workspace_bytes(int B, int H, int N, int D, int T);
 hipError_t run_pddp(const uint16_t *q, int64_t sb, int64_t sn, int64_t sh, int B, int H, int N,
                     int D, int T, int power_iters, bool whiten, int32_t *perm, void *ws,

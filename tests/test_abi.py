@@ -25,7 +25,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(s[0] for s in B.SIGNATURES) == names
@@ -192,3 +192,18 @@ def test_kv_idx_codec_argument_checks(lib):
     assert lib.mcs_kv_idx_decode(ctypes.byref(d), 128, mis, 10, FAKE, None) == 1
     big = desc(H=1, N=(1 << 19) + 1)
     assert lib.mcs_kv_idx_encode(ctypes.byref(big), 128, FAKE, 10, other, None) == 2
+
+
+def test_noalloc_validation_on_the_host(lib):
+    """mcs_pddp_group_noalloc checks its arguments, and that one head's
+    workspace fits the library's scratch, before it looks up the scratch or
+    launches anything (no GPU here)."""
+    d = desc(N=1000)
+    assert lib.mcs_pddp_group_noalloc(ctypes.byref(d), FAKE, 128, 16, 0, None, None) == 1
+    assert lib.mcs_pddp_group_noalloc(ctypes.byref(d), FAKE, 128, 16, 2, FAKE, None) == 1
+    assert b"flag" in lib.mcs_last_error()
+    assert lib.mcs_pddp_group_noalloc(ctypes.byref(d), FAKE, 128, 0, 0, FAKE, None) == 1
+    assert lib.mcs_pddp_group_noalloc(ctypes.byref(d), FAKE, 96, 16, 0, FAKE, None) == 2
+    big = desc(H=1, N=200000)
+    assert lib.mcs_pddp_group_noalloc(ctypes.byref(big), FAKE, 128, 16, 0, FAKE, None) == 2
+    assert b"scratch" in lib.mcs_last_error()

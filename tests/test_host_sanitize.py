@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CLANG = "/opt/rocm/llvm/bin/clang"
-KERNEL_OBJS = ["mcs_attention.o", "mcs_select.o", "mcs_pddp.o", "mcs_idxcode.o"]
+KERNEL_OBJS = ["mcs_attention.o", "mcs_select.o", "mcs_pddp.o", "mcs_idxcode.o", "mcs_scratch.o"]
 
 PROGRAM = r"""
 #include <stdint.h>
@@ -61,7 +61,8 @@ int main(void) {
       case 1: s = mcs_anchor_select_topk_workspace_size(&d, T, K, &n); break;
       case 2: s = mcs_kv_idx_bitmap_bytes(&d, T, &n); break;
       case 3: s = mcs_pddp_group(&d, ptr(), T, iters, ptr(), ptr(), (size_t)pick64(), NULL); break;
-      case 4: s = mcs_pddp_group_ex(&d, ptr(), T, iters, (uint32_t)rnd() & 3u, ptr(), ptr(), (size_t)pick64(), NULL); break;
+      case 4: s = (rnd() & 1) ? mcs_pddp_group_ex(&d, ptr(), T, iters, (uint32_t)rnd() & 3u, ptr(), ptr(), (size_t)pick64(), NULL)
+                              : mcs_pddp_group_noalloc(&d, ptr(), T, iters, (uint32_t)rnd() & 3u, ptr(), NULL); break;
       case 5: s = mcs_anchor_dense_lse(&d, ptr(), ptr(), ptr(), ptr(), ptr(), NULL); break;
       case 6: s = mcs_anchor_select_topk(&d, ptr(), ptr(), ptr(), ptr(), T, K, ptr(), ptr(), ptr(), (size_t)pick64(), NULL); break;
       case 7: s = mcs_residual(&d, ptr(), ptr(), ptr(), ptr(), ptr(), T, ptr(), K, ptr(), NULL); break;
