@@ -387,6 +387,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="wan480p")
     ap.add_argument("--density", type=int, default=None, help="override the density in percent")
+    ap.add_argument("--group-size", type=int, default=None, choices=[64, 128],
+                    help="override the query group (tile) size of the default bench")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -457,6 +459,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.density is not None:
         w = w.with_density(args.density)
+    if args.group_size is not None:
+        import dataclasses
+        w = dataclasses.replace(w, group_size=args.group_size)
     B, H, N, d, T, K, G = w.batch, w.heads, w.seqlen, w.head_dim, w.group_size, w.topk, w.groups
     R_STEPS = max(1, w.reuse_steps)
 
@@ -552,7 +557,7 @@ def main():
     achieved = value
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "attention_kernel<128,4,sparse> (mcs_sparse_apply)",
+                "traffic": traffic, "kernel": f"attention_kernel<{d},{T // 32},sparse> (mcs_sparse_apply)",
                 "per_launch_flop": flops, "avg_launch_ms": round(reuse_ms, 4)}
 
     out = {

@@ -43,9 +43,14 @@ struct AttnCfg {
 // exponentials may reach 2^8, which fp32 and bf16 hold exactly as well as 1.
 constexpr float kRescaleLog2 = 8.0f;
 
+// Waves per SIMD the LDS allows: one 8-wave (dense, 256-row) workgroup per
+// CU; two 4-wave ones (64.5 KB each); two 2-wave ones for 64-row groups,
+// whose two 32 KB stages cap them at two per CU as well (one wave per SIMD).
+template <int NW>
+constexpr int attn_waves_per_simd() { return NW == 4 ? 2 : 1; }
+
 template <int D, int NW, int MODE>
-// one 8-wave (dense, 256-row) or two 4-wave workgroups per CU
-__global__ __launch_bounds__(64 * NW, NW >= 8 ? 1 : 2) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_kernel(AttnArgs a) {
   // 128-key tiles on the 256-row dense path (one barrier and DMA wait per
   // 128 keys; its single workgroup per CU has the LDS for them), 64 keys
   // elsewhere

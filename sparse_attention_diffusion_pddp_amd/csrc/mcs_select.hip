@@ -42,8 +42,9 @@ struct MassCfg {
 
 template <int D, int NW>
 // four workgroups per CU (34.5 KB of LDS each at d = 128): at 128 VGPRs the
-// waves' exponentials and MFMAs overlap better than at two workgroups
-__global__ __launch_bounds__(64 * NW, 4) void mass_kernel(SelectArgs a) {
+// waves' exponentials and MFMAs overlap better than at two workgroups. With
+// 2-wave workgroups (64-row groups) the same four make two waves per SIMD.
+__global__ __launch_bounds__(64 * NW, NW >= 4 ? 4 : 2) void mass_kernel(SelectArgs a) {
   using C = MassCfg<D, NW>;
   // two stages as separate LDS objects, so the compiler can tell the stage
   // being filled by DMA from the one being read
