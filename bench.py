@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "reuse-step sparse attn eff. TFLOP/s @15% density + anchor-step ms (1 GPU)"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP64_TFLOPS = 78.6  # MI355X float64 (matrix and vector)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_apply_wan480p_traffic.json")
 KERNEL_SOURCES = ["mcs_attention.hip", "mcs_common.hpp", "mcs_lds.hpp"]
 
@@ -537,6 +538,7 @@ def main():
     torch.cuda.synchronize()
     reuse_warm_ms = we[0].elapsed_time(we[-1]) / (2 * R_STEPS)
     pddp_bytes = metrics.pddp_algorithmic_bytes(B, H, N, d, T)
+    pddp_flop = metrics.pddp_fp64_flops(B, H, N, d, T)
 
     # the same library's dense path (lse = NULL), the speedup denominator
     o2 = torch.empty_like(dq)
@@ -580,7 +582,10 @@ def main():
         "value_warm": round(flops / (reuse_warm_ms * 1e-3) / 1e12, 2),
         "pddp": {"ms": round(stage_ms["pddp"], 4), "algorithmic_bytes": pddp_bytes,
                  "GBps": round(pddp_bytes / (stage_ms["pddp"] * 1e-3) / 1e9, 1),
-                 "frac_hbm": round(pddp_bytes / (stage_ms["pddp"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                 "frac_hbm": round(pddp_bytes / (stage_ms["pddp"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                 "fp64_flop": pddp_flop,
+                 "fp64_TFLOPs": round(pddp_flop / (stage_ms["pddp"] * 1e-3) / 1e12, 2),
+                 "frac_fp64": round(pddp_flop / (stage_ms["pddp"] * 1e-3) / 1e12 / PEAK_FP64_TFLOPS, 4)},
         "anchor_step_ms": round(anchor_ms, 3),
         "anchor_stages_ms": {s: round(stage_ms[s], 3) for s in stages[:4]},
         "reuse_step_ms": round(reuse_ms, 4),

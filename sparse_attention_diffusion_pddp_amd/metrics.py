@@ -39,6 +39,22 @@ def pddp_algorithmic_bytes(batch, heads, seqlen, head_dim, group_size, elem_byte
     return batch * heads * (pddp_levels(seqlen, group_size) * seqlen * head_dim * elem_bytes + seqlen * 4)
 
 
+def pddp_fp64_flops(batch, heads, seqlen, head_dim, group_size, power_iters=16) -> int:
+    """float64 FLOPs of the grouping as this library computes it: the
+    second moments (the upper triangle of d x d, in 16 x 16 tiles, per
+    accumulated token: every token at the first level, the left children's
+    (about half) below), 16 matrix-vector products per split node, and one
+    projection of every token per level. 2 FLOPs per multiply-add."""
+    tiles = (head_dim // 16) * (head_dim // 16 + 1) // 2
+    per_token = tiles * 256
+    levels = pddp_levels(seqlen, group_size)
+    groups = -(-seqlen // group_size)
+    accumulated = seqlen + (levels - 1) * (seqlen // 2) if levels else 0
+    nodes = groups - 1  # every split node of a binary tree with `groups` leaves
+    macs = accumulated * per_token + nodes * power_iters * head_dim * head_dim + levels * seqlen * head_dim
+    return 2 * batch * heads * macs
+
+
 def kernel_speedup(t_dense, t_sparse, density):
     """Attention-kernel speedup rho = t_dense / t_sparse and efficiency eta = rho * s
     against the ideal 1/s speedup (paper landing page, Table 6)."""

@@ -74,3 +74,18 @@ def test_recall_and_rel_l1_formulas_match_the_oracle():
     assert abs(metrics.rel_l1(torch.from_numpy(x), torch.from_numpy(ref)) - O.rel_l1(x, ref)) < 1e-14
     assert metrics.matched_blocks(4914, 64) == 77 and metrics.matched_blocks(8190, 64) == 128
     assert metrics.matched_blocks(10, 64) == 1 and metrics.matched_blocks(96, 64) == 2
+
+
+def test_pddp_work_counts():
+    """Tree depth and the grouping's algorithmic bytes and float64 FLOPs,
+    against hand counts."""
+    from sparse_attention_diffusion_pddp_amd import metrics
+    assert metrics.pddp_levels(32760, 128) == 8      # 256 groups
+    assert metrics.pddp_levels(98304, 128) == 10     # 768 groups: 3 x 2^8
+    assert metrics.pddp_levels(64000, 128) == 9      # 500 groups
+    assert metrics.pddp_levels(128, 128) == 0 and metrics.pddp_levels(129, 128) == 1
+    assert metrics.pddp_algorithmic_bytes(1, 1, 300, 64, 128) == 2 * 300 * 64 * 2 + 300 * 4  # 3 groups: 2 levels
+    # N = 300, d = 32, T = 128: levels 2, groups 3 (2 split nodes); 3 tiles of 16 x 16 per token;
+    # accumulated tokens 300 + 150 = 450
+    want = 2 * (450 * 3 * 256 + 2 * 16 * 32 * 32 + 2 * 300 * 32)
+    assert metrics.pddp_fp64_flops(1, 1, 300, 32, 128) == want
