@@ -814,23 +814,37 @@ __global__ __launch_bounds__(256) void project_kernel(PddpArgs a) {
   }
   double *proj = a.proj + (int64_t)bh * a.N;
   int32_t *tmp = a.tmp + (int64_t)bh * a.N;
-  for (int i0 = wave * TPW; i0 < c.len; i0 += 4 * TPW) {
-    const int i = i0 + tw;
-    const bool ok = i < c.len;
-    const int pos = c.off + (ok ? i : 0);
-    const int tok = cur[pos];
-    const u32x4 v = *(const u32x4 *)(qh + (int64_t)tok * a.sn + sub * 8);
-    double p = 0.0;
+  // the chunk's tokens in one coalesced read, then UNR rows in flight per
+  // lane group: the row loads no longer wait one by one behind index loads
+  __shared__ int32_t toks[kPChunk];
+  for (int i = tid; i < c.len; i += 256) toks[i] = cur[c.off + i];
+  __syncthreads();
+  constexpr int TPB = 4 * TPW;  // tokens per block step
+  constexpr int UNR = 4;
+  for (int i0 = wave * TPW; i0 < c.len; i0 += UNR * TPB) {
+    u32x4 v[UNR];
+    int tk[UNR];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      p += ((double)bf16_to_f32(v[m] & 0xffffu) - m8[2 * m]) * u8[2 * m];
-      p += ((double)bf16_to_f32(v[m] >> 16) - m8[2 * m + 1]) * u8[2 * m + 1];
+    for (int u = 0; u < UNR; ++u) {
+      const int i = i0 + u * TPB + tw;
+      tk[u] = toks[i < c.len ? i : 0];
+      v[u] = *(const u32x4 *)(qh + (int64_t)tk[u] * a.sn + sub * 8);
     }
 #pragma unroll
-    for (int s = LPT / 2; s > 0; s >>= 1) p += __shfl_xor(p, s);
-    if (ok && sub == 0) {
-      proj[pos] = p;
-      tmp[pos] = tok;
+    for (int u = 0; u < UNR; ++u) {
+      const int i = i0 + u * TPB + tw;
+      double p = 0.0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        p += ((double)bf16_to_f32(v[u][m] & 0xffffu) - m8[2 * m]) * u8[2 * m];
+        p += ((double)bf16_to_f32(v[u][m] >> 16) - m8[2 * m + 1]) * u8[2 * m + 1];
+      }
+#pragma unroll
+      for (int s = LPT / 2; s > 0; s >>= 1) p += __shfl_xor(p, s);
+      if (i < c.len && sub == 0) {
+        proj[c.off + i] = p;
+        tmp[c.off + i] = tk[u];
+      }
     }
   }
 }
@@ -919,9 +933,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(PddpArgs a) {
 // single barrier that gives it the counts of the positions before it.
 constexpr int kSplitCopies = 8;
 
-template <int KPT>
-__global__ __launch_bounds__(kSplitThreads) void split_reg_kernel(PddpArgs a) {
-  constexpr int NW = kSplitThreads / 64;
+template <int NTH, int KPT>
+__global__ __launch_bounds__(NTH) void split_reg_kernel(PddpArgs a) {
+  constexpr int NW = NTH / 64;
   constexpr int SEG = 64 * KPT;
   __shared__ uint32_t hc[kSplitCopies * 257];
   __shared__ uint32_t hist[256];
@@ -952,7 +966,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_reg_kernel(PddpArgs a) {
 #pragma unroll 1
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 56 - 8 * pass;
-    for (int i = tid; i < kSplitCopies * 257; i += kSplitThreads) hc[i] = 0;
+    for (int i = tid; i < kSplitCopies * 257; i += NTH) hc[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < KPT; ++k)
@@ -1024,16 +1038,21 @@ __global__ __launch_bounds__(kSplitThreads) void split_reg_kernel(PddpArgs a) {
   }
 }
 
-// the split of one level: register keys when its largest node fits
+// the split of one level: register keys when its largest node fits. The
+// top levels have few nodes (one or two per head), so nodes above 8192
+// tokens get more threads (fewer keys per thread, more waves hiding each
+// pass's latency) as far as the registers allow without spilling: 1024
+// threads of 16 keys, then 768 threads of 43; the result does not depend
+// on the count.
 hipError_t launch_split(const PddpArgs &a, const PLevel &L, int BH, hipStream_t s) {
   const dim3 g(L.nnodes, BH), b(kSplitThreads);
-  if (L.maxn <= 512) hipLaunchKernelGGL(split_reg_kernel<1>, g, b, 0, s, a);
-  else if (L.maxn <= 512 * 2) hipLaunchKernelGGL(split_reg_kernel<2>, g, b, 0, s, a);
-  else if (L.maxn <= 512 * 4) hipLaunchKernelGGL(split_reg_kernel<4>, g, b, 0, s, a);
-  else if (L.maxn <= 512 * 8) hipLaunchKernelGGL(split_reg_kernel<8>, g, b, 0, s, a);
-  else if (L.maxn <= 512 * 16) hipLaunchKernelGGL(split_reg_kernel<16>, g, b, 0, s, a);
-  else if (L.maxn <= 512 * 32) hipLaunchKernelGGL(split_reg_kernel<32>, g, b, 0, s, a);
-  else if (L.maxn <= 512 * 64) hipLaunchKernelGGL(split_reg_kernel<64>, g, b, 0, s, a);
+  if (L.maxn <= 512) hipLaunchKernelGGL((split_reg_kernel<kSplitThreads, 1>), g, b, 0, s, a);
+  else if (L.maxn <= 512 * 2) hipLaunchKernelGGL((split_reg_kernel<kSplitThreads, 2>), g, b, 0, s, a);
+  else if (L.maxn <= 512 * 4) hipLaunchKernelGGL((split_reg_kernel<kSplitThreads, 4>), g, b, 0, s, a);
+  else if (L.maxn <= 512 * 8) hipLaunchKernelGGL((split_reg_kernel<kSplitThreads, 8>), g, b, 0, s, a);
+  else if (L.maxn <= 1024 * 16) hipLaunchKernelGGL((split_reg_kernel<1024, 16>), g, dim3(1024), 0, s, a);
+  else if (L.maxn <= 768 * 43) hipLaunchKernelGGL((split_reg_kernel<768, 43>), g, dim3(768), 0, s, a);
+  else if (L.maxn <= 512 * 64) hipLaunchKernelGGL((split_reg_kernel<kSplitThreads, 64>), g, b, 0, s, a);
   else hipLaunchKernelGGL(split_kernel, g, b, 0, s, a);
   return hipGetLastError();
 }
