@@ -106,7 +106,9 @@ const char *mcs_last_error(void);
  *   perm      out, int32 [B][H][N].
  *   ws        device workspace of at least mcs_pddp_group_workspace_size()
  *             bytes; contents are scratch.
- * perm and ws must not overlap q or each other.
+ * perm and ws must not overlap q or each other. batch * heads above 65535
+ * is MCS_ERR_UNSUPPORTED (for this call, its workspace query, _ex and
+ * _noalloc).
  * ------------------------------------------------------------------------ */
 mcs_status_t mcs_pddp_group_workspace_size(const mcs_attn_desc_t *desc, int32_t group_size,
                                            size_t *bytes);

@@ -111,6 +111,16 @@ mcs_status_t check_ptr(const void *p, const char *name) {
   return ok();
 }
 
+// the grouping kernels run a grid row per (batch, head): at most 65535
+constexpr int64_t kMaxPddpHeads = 65535;
+
+mcs_status_t check_pddp_heads(const mcs_attn_desc_t *d) {
+  if ((int64_t)d->batch * d->heads > kMaxPddpHeads)
+    return fail(MCS_ERR_UNSUPPORTED, "batch*heads %lld above the grouping's %lld",
+                (long long)d->batch * d->heads, (long long)kMaxPddpHeads);
+  return ok();
+}
+
 mcs_status_t check_group(int32_t T) {
   if (T != 64 && T != 128) return fail(MCS_ERR_UNSUPPORTED, "group_size %d not supported (64 or 128)", T);
   return ok();
@@ -179,6 +189,7 @@ const char *mcs_last_error(void) { return g_last_error.c_str(); }
 mcs_status_t mcs_pddp_group_workspace_size(const mcs_attn_desc_t *desc, int32_t group_size,
                                            size_t *bytes) {
   MCS_TRY(check_desc(desc));
+  MCS_TRY(check_pddp_heads(desc));
   MCS_TRY(check_group(group_size));
   if (!bytes) return fail(MCS_ERR_INVALID_ARGUMENT, "bytes is NULL");
   *bytes = mcs::pddp_workspace_bytes(desc->batch, desc->heads, desc->seqlen, desc->head_dim, group_size);
@@ -189,6 +200,7 @@ mcs_status_t mcs_pddp_group_ex(const mcs_attn_desc_t *desc, const void *q, int32
                                int32_t power_iters, uint32_t flags, int32_t *perm, void *ws,
                                size_t ws_bytes, mcs_stream_t stream) {
   MCS_TRY(check_desc(desc));
+  MCS_TRY(check_pddp_heads(desc));
   MCS_TRY(check_group(group_size));
   MCS_TRY(check_tensor(q, "q"));
   MCS_TRY(check_ptr(perm, "perm"));
@@ -211,6 +223,7 @@ mcs_status_t mcs_pddp_group_ex(const mcs_attn_desc_t *desc, const void *q, int32
 mcs_status_t mcs_pddp_group_noalloc(const mcs_attn_desc_t *desc, const void *q, int32_t group_size,
                                     int32_t power_iters, uint32_t flags, int32_t *perm, mcs_stream_t stream) {
   MCS_TRY(check_desc(desc));
+  MCS_TRY(check_pddp_heads(desc));
   MCS_TRY(check_group(group_size));
   MCS_TRY(check_tensor(q, "q"));
   MCS_TRY(check_ptr(perm, "perm"));

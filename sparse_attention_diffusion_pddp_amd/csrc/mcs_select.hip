@@ -513,13 +513,12 @@ __global__ __launch_bounds__(256) void block_sum_kernel(const float *mass, int N
   }
 }
 
-// kv_idx row = the chosen blocks' keys, block by block (blocks ascending)
+// kv_idx row = the chosen blocks' keys, block by block (blocks ascending);
+// one workgroup per row (a 1-D grid: rows may exceed a grid's y extent)
 __global__ __launch_bounds__(256) void block_expand_kernel(const int32_t *bidx, int nb, int blk, int32_t *kv_idx) {
-  const int64_t row = blockIdx.y;
+  const int64_t row = blockIdx.x;
   const int K = nb * blk;
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= K) return;
-  kv_idx[row * K + i] = bidx[row * nb + i / blk] * blk + i % blk;
+  for (int i = threadIdx.x; i < K; i += 256) kv_idx[row * K + i] = bidx[row * nb + i / blk] * blk + i % blk;
 }
 
 hipError_t launch_select_blocks(const float *mass, int64_t rows, int N, int blk, int nb, int32_t *kv_idx, void *ws,
@@ -541,9 +540,7 @@ hipError_t launch_select_blocks(const float *mass, int64_t rows, int N, int blk,
   a.K = nb;
   e = launch_topk(a, s);
   if (e != hipSuccess) return e;
-  const int K = nb * blk;
-  hipLaunchKernelGGL(block_expand_kernel, dim3((unsigned)((K + 255) / 256), (unsigned)rows), dim3(256), 0, s, bidx,
-                     nb, blk, kv_idx);
+  hipLaunchKernelGGL(block_expand_kernel, dim3((unsigned)rows), dim3(256), 0, s, bidx, nb, blk, kv_idx);
   return hipGetLastError();
 }
 

@@ -207,3 +207,28 @@ def test_noalloc_validation_on_the_host(lib):
     big = desc(H=1, N=200000)
     assert lib.mcs_pddp_group_noalloc(ctypes.byref(big), FAKE, 128, 16, 0, FAKE, None) == 2
     assert b"scratch" in lib.mcs_last_error()
+
+
+def test_grouping_refuses_more_heads_than_its_grid_rows(lib):
+    """The grouping kernels run one grid row per (batch, head); more than
+    65535 heads is refused on the host, for every grouping call."""
+    d = B.Desc(2, 40000, 64, 128, 40000 * 64 * 128, 128, 64 * 128, 0.088)
+    n = ctypes.c_size_t()
+    assert lib.mcs_pddp_group_workspace_size(ctypes.byref(d), 128, ctypes.byref(n)) == 2
+    assert b"65535" in lib.mcs_last_error()
+    assert lib.mcs_pddp_group(ctypes.byref(d), FAKE, 128, 16, FAKE, FAKE, 1 << 40, None) == 2
+    assert lib.mcs_pddp_group_noalloc(ctypes.byref(d), FAKE, 128, 16, 0, FAKE, None) == 2
+
+
+def test_select_blocks_validation_on_the_host(lib):
+    d = desc(N=1000)
+    n = ctypes.c_size_t()
+    assert lib.mcs_select_blocks_workspace_size(ctypes.byref(d), 128, 64, 15, ctypes.byref(n)) == 0
+    assert n.value > 0
+    assert lib.mcs_select_blocks_workspace_size(ctypes.byref(d), 128, 96, 2, ctypes.byref(n)) == 2  # not a multiple of 64
+    assert lib.mcs_select_blocks_workspace_size(ctypes.byref(d), 128, 64, 16, ctypes.byref(n)) == 1  # 15 full blocks
+    assert lib.mcs_select_blocks_workspace_size(ctypes.byref(d), 128, 64, 0, ctypes.byref(n)) == 1
+    short = desc(N=50)
+    assert lib.mcs_select_blocks_workspace_size(ctypes.byref(short), 128, 64, 1, ctypes.byref(n)) == 1
+    assert b"full block" in lib.mcs_last_error()
+    assert lib.mcs_select_blocks(ctypes.byref(d), FAKE, 128, 64, 4, FAKE, FAKE, 16, None) == 3  # workspace too small

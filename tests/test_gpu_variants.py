@@ -118,3 +118,32 @@ def test_variant_table_is_ordered_like_the_pages(res):
         if key != ("pddp", "token"):
             assert best["recall"] >= x["recall"] - 1e-6, key
             assert best["rel_l1_sparse_anchor"] <= x["rel_l1_sparse_anchor"] + 1e-6, key
+
+
+@pytest.mark.parametrize("block,nb", [(64, 15), (64, 1), (128, 3), (192, 5)])
+def test_select_blocks_exact_answers(lib, block, nb):
+    """Masses that are multiples of 1/8 below 2^10, so every fp32 block sum
+    is exact: the chosen blocks are the largest sums, lowest block first
+    among equal ones (many ties by construction), never the partial block
+    (which gets the largest masses), expanded block by block ascending."""
+    B_, H, N, T = 2, 3, 1000, 128
+    G = -(-N // T)
+    rng = np.random.default_rng(block + nb)
+    mass = (rng.integers(0, 6, size=(B_, H, G, N)) / 8.0).astype(np.float32)
+    nfull = N // block
+    mass[..., nfull * block:] = 100.0
+    # equal sums in some rows: copy block 0 over block 2
+    mass[0, 1, :, 2 * block:3 * block] = mass[0, 1, :, :block]
+    q = torch.zeros((B_, N, H, 64), dtype=torch.bfloat16, device="cuda")
+    desc = mcs.desc_for(q)
+    got = torch.empty((B_, H, G, nb * block), dtype=torch.int32, device="cuda")
+    mcs.select_blocks(desc, torch.from_numpy(mass).cuda(), T, block, nb, got)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    for b in range(B_):
+        for h in range(H):
+            for g in range(G):
+                sums = mass[b, h, g, :nfull * block].astype(np.float64).reshape(nfull, block).sum(1)
+                order = sorted(range(nfull), key=lambda x: (-sums[x], x))[:nb]
+                want = [c * block + t for c in sorted(order) for t in range(block)]
+                assert got[b, h, g].tolist() == want, (b, h, g)
