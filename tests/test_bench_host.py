@@ -67,3 +67,16 @@ def test_committed_traffic_is_ignored_once_the_kernel_changes(monkeypatch):
 def test_schedule_input_sets(anchors, expect):
     for step, k in expect.items():
         assert bench.input_set(step, anchors) == k, step
+
+
+def test_cpu_baseline_times_the_cpp_oracle():
+    """The baseline leg runs the C++ oracle's reuse driver on a bounded
+    sample and reports its worker count as cores."""
+    from oracle import cpp
+    from sparse_attention_diffusion_pddp_amd import synth
+    w = synth.small_workload(1200, heads=2, head_dim=64, group_size=128, density_pct=10)
+    out = bench.cpu_baseline(w, 0.2, seed=3, n_groups=4)
+    assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s"
+    assert out["cores"] == cpp.default().threads >= 1
+    assert out["value"] > 0 and "first 4 query groups of head 0" in out["sample"]
+    assert "C++ float64 oracle" in out["sample"]
