@@ -334,6 +334,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   });
 }
 
+// Indices staged in LDS before the row's output is written: the whole row
+// (K <= N) for the smaller kernels, else 12,288 indices (48 KB, two 512-thread
+// workgroups per CU), or 16,384 (64 KB) for the 768-thread kernel, which runs
+// one workgroup per CU.
+template <int NTH, int KPT>
+constexpr int topk_stage_cap() {
+  return NTH == 768 ? 16384 : (NTH * KPT < 12288 ? NTH * KPT : 12288);
+}
+
 // Rows of up to NTH * KPT keys: the whole row is read once into registers
 // (wave w holds the contiguous segment [w * 64 * KPT, (w + 1) * 64 * KPT),
 // lane l the keys at l, l + 64, ...), every digit is resolved from the
@@ -343,10 +352,12 @@ template <int NTH, int KPT>
 __global__ __launch_bounds__(NTH) void topk_reg_kernel(SelectArgs a) {
   constexpr int NW = NTH / 64;
   constexpr int SEG = 64 * KPT;
+  constexpr int SCAP = topk_stage_cap<NTH, KPT>();
   __shared__ uint32_t hc[kHCopies * 513];
   __shared__ uint32_t hist[512];
   __shared__ uint32_t gt_cnt[NW], eq_cnt[NW];
   __shared__ uint32_t sel_digit, sel_above;
+  __shared__ int32_t stage[SCAP];
 
   const int row = xcd_remap(blockIdx.x, gridDim.x);  // (bh, g) flattened
   const float *A = a.mass + (int64_t)row * a.N;
@@ -418,12 +429,16 @@ __global__ __launch_bounds__(NTH) void topk_reg_kernel(SelectArgs a) {
   }
   const uint32_t tau = prefix;
   const uint32_t need = remaining;
-  // the segments' counts above and equal to tau
+  // the segments' counts above and equal to tau (tau through an empty asm:
+  // the partitions below then make their own comparisons instead of keeping
+  // these 2 * KPT flags live across the barrier)
+  uint32_t tau_cnt = tau;
+  asm volatile("" : "+v"(tau_cnt));
   uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
-    gt += u[k] > tau ? 1u : 0u;
-    eq += u[k] == tau ? 1u : 0u;
+    gt += u[k] > tau_cnt ? 1u : 0u;
+    eq += u[k] == tau_cnt ? 1u : 0u;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -442,6 +457,46 @@ __global__ __launch_bounds__(NTH) void topk_reg_kernel(SelectArgs a) {
     written += gt_cnt[w] + (e < room ? e : room);
     ties += e;
   }
+  uint32_t eq_all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) eq_all += eq_cnt[w];
+  if (eq_all == need) {
+    // Every key equal to tau is kept (the usual case: the K-th largest mass
+    // is unique), so the selection is simply u >= tau, K keys in all. A
+    // key's position is its wave's offset plus the selected keys before it
+    // in (k, lane) order. With K <= SCAP the indices gather in LDS and the
+    // row is written by all threads in order, 256 contiguous bytes a wave.
+    // (tau passes through an empty asm so that these comparisons are not
+    // merged with the counts' above, whose 128 flags would then stay live.)
+    uint32_t tau_ge = tau;
+    asm volatile("" : "+v"(tau_ge));
+    if (a.K <= SCAP) {
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) {
+        const bool sel = u[k] >= tau_ge;
+        const uint64_t m = __ballot(sel);
+        const uint32_t pos = written + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (sel && pos < (uint32_t)a.K) stage[pos] = j0 + 64 * k;
+        written += (uint32_t)__popcll(m);
+      }
+      __syncthreads();
+      for (int i = tid; i < a.K; i += NTH) out[i] = stage[i];
+    } else {
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) {
+        const bool sel = u[k] >= tau_ge;
+        const uint64_t m = __ballot(sel);
+        const uint32_t pos = written + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (sel && pos < (uint32_t)a.K) out[pos] = j0 + 64 * k;
+        written += (uint32_t)__popcll(m);
+      }
+    }
+    return;
+  }
+  // Some keys equal to tau are left out: they are taken in ascending index
+  // order until `need` of them are in.
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const bool g = u[k] > tau;
