@@ -10,7 +10,11 @@ increasing in k_j (adjacent grid values differ in mass by 0.8%, far above
 fp32 rounding), and many keys share each value. The top-K are then the keys
 of largest k_j, lowest index first among equals (the pages' tie rule as this
 library reads it), stored ascending. With all keys equal, every mass ties
-and the answer is the first K indices."""
+and the answer is the first K indices. Those rows leave keys equal to the
+K-th largest out, so the partition ranks ties; rows of distinct scores
+(two key dimensions) take its plain form, whose indices are staged in LDS
+up to a capacity and written straight out beyond it: both are covered at
+each capacity's edge."""
 import numpy as np
 import pytest
 import torch
@@ -114,3 +118,51 @@ def test_topk_row_one_past_segments_exact_buffer(lib, N):
     want = expected(kcol, K)
     for g in range(G):
         assert np.array_equal(got[g], want), f"N={N} group {g}"
+
+
+def run_select_2d(a_col, b_col, K):
+    """Queries (16, 1/16, 0, ...) and keys (a_j, b_j, 0, ...): the score is
+    16 a_j + b_j / 16, exact in the MFMA's fp32 sums."""
+    N = a_col.shape[0]
+    q = torch.zeros((1, N, 1, D), dtype=torch.bfloat16)
+    q[0, :, 0, 0] = 16.0
+    q[0, :, 0, 1] = 1.0 / 16.0
+    k = torch.zeros((1, N, 1, D), dtype=torch.bfloat16)
+    k[0, :, 0, 0] = torch.from_numpy(a_col).to(torch.bfloat16)
+    k[0, :, 0, 1] = torch.from_numpy(b_col).to(torch.bfloat16)
+    assert torch.equal(k[0, :, 0, 0].double(), torch.from_numpy(a_col))
+    assert torch.equal(k[0, :, 0, 1].double(), torch.from_numpy(b_col))
+    q, k = q.cuda(), k.cuda()
+    G = -(-N // T)
+    lse = torch.zeros((1, 1, N), dtype=torch.float32, device="cuda")
+    perm = torch.arange(N, dtype=torch.int32, device="cuda").reshape(1, 1, N)
+    idx = torch.empty((1, 1, G, K), dtype=torch.int32, device="cuda")
+    desc = mcs.desc_for(q)
+    ws = torch.empty(mcs.select_workspace_size(desc, T, K), dtype=torch.uint8, device="cuda")
+    mcs.anchor_select_topk(q, k, lse, perm, T, K, idx, ws=ws)
+    torch.cuda.synchronize()
+    return idx[0, 0].cpu().numpy()
+
+
+# Distinct masses at the top of the row, so the K-th largest is unique and
+# the partition takes its plain u >= tau form: with the indices staged in
+# LDS (K at the stage's capacity: 4096 for 8 keys a thread, 12288 on 512
+# threads, 16384 on 768) and written straight out (one key more).
+@pytest.mark.parametrize("N,K", [(4000, 4000), (32760, 12288), (32760, 12289), (60000, 12288), (60000, 12289),
+                                 (98304, 16384), (98304, 16385)])
+def test_topk_distinct_masses_both_partition_outputs(lib, N, K):
+    print(f"\n[topk distinct N={N} K={K}]", flush=True)
+    rng = np.random.default_rng(N + K)
+    # codes 256 A + B, A in [-128, 127], B in [0, 255]: 65536 distinct scores
+    # (256 A + B) / 512, 2.4e-4 apart in scale * score; rows longer than
+    # 65536 repeat the lowest code, far below the K-th largest
+    codes = rng.permutation(65536)[:min(N, 65536)]
+    if N > 65536:
+        codes = np.concatenate([codes, np.zeros(N - 65536, dtype=codes.dtype)])
+        codes = codes[rng.permutation(N)]
+    A, B = codes // 256 - 128, codes % 256
+    got = run_select_2d(A / 32.0, B / 32.0, K)
+    want = np.sort(np.argsort(-codes, kind="stable")[:K])
+    assert codes[np.argsort(-codes, kind="stable")[K - 1]] > 0, "the K-th largest is above the repeated code"
+    for g in range(got.shape[0]):
+        assert np.array_equal(got[g], want), f"N={N} K={K} group {g}"
