@@ -104,6 +104,30 @@ def write_traffic(fetch_dir, write_dir, fetch_copy_dir, write_copy_dir, kernel="
     print(json.dumps(out))
 
 
+def gemm_reference(n: int = 16384, reps: int = 4) -> dict:
+    """What a large dense bf16 GEMM from the platform library (torch.matmul,
+    hipBLASLt) sustains on this GPU, warm: a practical MFMA ceiling beside the
+    datasheet peak. Both operands are plain contiguous 2-D tensors."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    a = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16).contiguous()
+    b = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16).contiguous()
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return {"tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4), "shape": [n, n, n],
+            "lib": "torch.matmul bf16 (hipBLASLt), warm"}
+
+
 def cpu_baseline(w, seconds: float, seed: int, n_groups: int = 64):
     """The oracle, untuned, timed on the host on a bounded sample of the reuse
     step: the first ``n_groups`` query groups of head 0, through the C++
@@ -557,10 +581,12 @@ def main():
 
     traffic = load_traffic(flops)
     achieved = value
+    gemm = gemm_reference()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": f"attention_kernel<{d},{T // 32},sparse> (mcs_sparse_apply)",
-                "per_launch_flop": flops, "avg_launch_ms": round(reuse_ms, 4)}
+                "per_launch_flop": flops, "avg_launch_ms": round(reuse_ms, 4),
+                "frac_of_gemm_ref": round(achieved / gemm["tflops"], 4)}
 
     out = {
         "metric": METRIC,
@@ -597,6 +623,7 @@ def main():
         "anchor_overhead_density_points": round(metrics.anchor_overhead_points(anchor_only, dense_ms), 3),
         "pddp_ms_amortized_2_per_40": round(metrics.amortized_grouping_ms(stage_ms["pddp"]), 4),
         "roofline": roofline,
+        "gemm_ref": gemm,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.seed)
