@@ -40,11 +40,16 @@ struct MassCfg {
   static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "loader mapping");
 };
 
-template <int D, int NW>
-// four workgroups per CU (34.5 KB of LDS each at d = 128): at 128 VGPRs the
-// waves' exponentials and MFMAs overlap better than at two workgroups. With
-// 2-wave workgroups (64-row groups) the same four make two waves per SIMD.
-__global__ __launch_bounds__(64 * NW, NW >= 4 ? 4 : 2) void mass_kernel(SelectArgs a) {
+// GPW groups per workgroup, WPG waves (32 rows each) per group. 128-row
+// groups run two to a workgroup: the eight waves share each K tile's DMA,
+// and at 128 VGPRs two such workgroups fill a CU (four waves per SIMD):
+// select 4.6% faster than one group per workgroup at the same occupancy,
+// identical indices (randomised-order A/B in one process); four groups per
+// workgroup (one per CU) were 1.9% slower than one. 64-row groups keep one
+// 2-wave group per workgroup, four per CU (two waves per SIMD).
+template <int D, int WPG, int GPW>
+__global__ __launch_bounds__(64 * WPG * GPW, WPG * GPW >= 4 ? 4 : 2) void mass_kernel(SelectArgs a) {
+  constexpr int NW = WPG * GPW;
   using C = MassCfg<D, NW>;
   // two stages as separate LDS objects, so the compiler can tell the stage
   // being filled by DMA from the one being read
@@ -52,41 +57,45 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 4 : 2) void mass_kernel(SelectAr
   __shared__ __attribute__((aligned(1024))) bf16_t st1[C::KT * D];
   __shared__ float partial[2][NW][C::KT];
 
+  const int sets = (a.G + GPW - 1) / GPW;  // workgroups per head
   const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = work / a.G;
-  const int g = work - bh * a.G;
+  const int bh = work / sets;
+  const int gs = work - bh * sets;
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = wave % WPG;               // wave within its group
+  const int g = GPW * gs + wave / WPG;     // this wave's group (past G: none, rows masked)
+  const bool gvalid = g < a.G;
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const bf16_t *qb = a.q + head_off;
   const int32_t *pr = a.perm + (int64_t)bh * a.N;
   const float *lse = a.lse + (int64_t)bh * a.N;
-  const int row0 = g * a.T;
+  const int row0 = (gvalid ? g : 0) * a.T;
   const uint32_t row_bytes = (uint32_t)a.sn * 2u;
   const uint32_t extent = (uint32_t)(a.N - 1) * row_bytes + D * 2;
   const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(a.k + head_off, extent);
 
-  // A-operand rows: query wave*32 + l32 of the group
+  // A-operand rows: query wg*32 + l32 of the group
   bf16x8 qf[D / 16];
   {
-    const int r = wave * 32 + l32;
+    const int r = wg * 32 + l32;
     const int pos = row0 + r;
     const bool ok = r < a.T && pos < a.N;
     const bf16_t *qrow = qb + (int64_t)pr[ok ? pos : row0] * a.sn + 8 * hh;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = *(const bf16x8 *)(qrow + 16 * s);
   }
-  // accumulator rows held by this lane: wave*32 + 8*(v/4) + 4*hh + (v%4)
+  // accumulator rows held by this lane: wg*32 + 8*(v/4) + 4*hh + (v%4)
   float l2[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int r = wave * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+    const int r = wg * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
     const int pos = row0 + r;
-    const bool ok = r < a.T && pos < a.N;
+    const bool ok = gvalid && r < a.T && pos < a.N;
     l2[v] = ok ? lse[pr[pos]] * kLog2e : 1.0e30f;  // invalid row: P = 0
   }
   const float c2 = a.scale_log2;
@@ -107,13 +116,17 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 4 : 2) void mass_kernel(SelectAr
     }
   };
 
-  float *mass_row = a.mass + ((int64_t)bh * a.G + g) * a.N;
-  auto finish = [&](int t) {  // tile t's column sums over the waves, fixed order
-    if (tid < C::KT) {
-      const int key = t * C::KT + tid;
+  // thread fg * KT + fk finishes key fk of the tile for group GPW*gs + fg
+  const int fg = tid / C::KT;
+  const int fk = tid - fg * C::KT;
+  const bool fval = fg < GPW && GPW * gs + fg < a.G;
+  float *mass_row = a.mass + ((int64_t)bh * a.G + (GPW * gs + fg)) * a.N;
+  auto finish = [&](int t) {  // tile t's column sums over the group's waves, fixed order
+    if (fval) {
+      const int key = t * C::KT + fk;
       float s = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) s += partial[t & 1][w][tid];
+      for (int w = 0; w < WPG; ++w) s += partial[t & 1][WPG * fg + w][fk];
       if (key < a.N) mass_row[key] = s;
     }
   };
@@ -511,10 +524,10 @@ __global__ __launch_bounds__(NTH) void topk_reg_kernel(SelectArgs a) {
   }
 }
 
-template <int D, int NW>
+template <int D, int WPG, int GPW>
 static hipError_t launch_mass(const SelectArgs &a, hipStream_t s) {
-  const int nblocks = a.B * a.H * a.G;
-  hipLaunchKernelGGL((mass_kernel<D, NW>), dim3(nblocks), dim3(64 * NW), 0, s, a);
+  const int nblocks = a.B * a.H * ((a.G + GPW - 1) / GPW);
+  hipLaunchKernelGGL((mass_kernel<D, WPG, GPW>), dim3(nblocks), dim3(64 * WPG * GPW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -536,10 +549,10 @@ hipError_t launch_select(int head_dim, const SelectArgs &a, hipStream_t s) {
   const int nblocks = a.B * a.H * a.G;
   if (nblocks <= 0) return hipSuccess;
   hipError_t e;
-  if (head_dim == 128 && a.T == 128) e = launch_mass<128, 4>(a, s);
-  else if (head_dim == 128 && a.T == 64) e = launch_mass<128, 2>(a, s);
-  else if (head_dim == 64 && a.T == 128) e = launch_mass<64, 4>(a, s);
-  else if (head_dim == 64 && a.T == 64) e = launch_mass<64, 2>(a, s);
+  if (head_dim == 128 && a.T == 128) e = launch_mass<128, 4, 2>(a, s);
+  else if (head_dim == 128 && a.T == 64) e = launch_mass<128, 2, 1>(a, s);
+  else if (head_dim == 64 && a.T == 128) e = launch_mass<64, 4, 2>(a, s);
+  else if (head_dim == 64 && a.T == 64) e = launch_mass<64, 2, 1>(a, s);
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
   return launch_topk(a, s);
