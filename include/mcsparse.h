@@ -277,7 +277,9 @@ mcs_status_t mcs_kv_idx_decode(const mcs_attn_desc_t *desc, int32_t group_size, 
  *                         (a side stream). It first waits for the last store
  *                         of layer l, on whatever stream that ran, so a
  *                         store and a prefetch of one layer may be enqueued
- *                         on different streams. If the slot was acquired
+ *                         on different streams. It also waits for the
+ *                         slot's previous prefetch, so two prefetches into
+ *                         one slot never write it at once. If the slot was acquired
  *                         since its last prefetch, the copy also waits for
  *                         all work enqueued so far on the acquiring stream,
  *                         so enqueue the slot's reader kernels before the

@@ -154,6 +154,10 @@ mcs_status_t mcs_rcache_prefetch(mcs_rcache_t *c, int32_t layer, mcs_stream_t st
     HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, c->freed[s], 0), "mcs_rcache_prefetch");
     c->acquired[s] = false;
   }
+  // an earlier prefetch into this slot, on whatever stream, has finished
+  // writing it (otherwise the two copies would race on the slot)
+  if (c->slot_layer[s] >= 0)
+    HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, c->ready[s], 0), "mcs_rcache_prefetch");
   // the blob's last store has landed in host memory
   HIP_TRY(hipStreamWaitEvent((hipStream_t)stream, c->store_done[layer], 0), "mcs_rcache_prefetch");
   HIP_TRY(hipMemcpyAsync(c->slot[s], c->host + (size_t)layer * c->bytes, c->bytes, hipMemcpyHostToDevice,

@@ -301,3 +301,30 @@ def test_rcache_store_and_prefetch_on_different_streams(lib):
     assert torch.equal(got, first)
     assert torch.equal(got2, second)
     cache.close()
+
+
+def test_rcache_two_prefetches_into_one_slot_on_different_streams(lib):
+    """Layers 0 and 2 share slot 0. Their prefetches are enqueued on two
+    streams with no acquire between them: the second waits for the first, so
+    the slot ends up holding layer 2 and acquire(2) reads it whole."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    nbytes = 32 << 20
+    l0 = torch.randint(0, 2**15, (nbytes // 2,), dtype=torch.int16, device="cuda")
+    l2 = torch.randint(0, 2**15, (nbytes // 2,), dtype=torch.int16, device="cuda")
+    cache = mcs.RCache(3, nbytes)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    cache.store(0, l0, s1)
+    cache.store(2, l2, s1)
+    torch.cuda.synchronize()
+    cache.prefetch(0, s1)
+    cache.prefetch(2, s2)
+    ptr = cache.acquire(2, compute)
+    got = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    assert hip.hipMemcpyAsync(ctypes.c_void_p(got.data_ptr()), ctypes.c_void_p(ptr), nbytes, 3,
+                              ctypes.c_void_p(compute.cuda_stream)) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(got, l2)
+    cache.close()
