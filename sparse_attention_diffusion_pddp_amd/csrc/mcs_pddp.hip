@@ -308,6 +308,25 @@ inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // doubles per moment block: the upper-triangle tiles of S, then s
 constexpr int moment_doubles(int D) { return (D / 16) * (D / 16 + 1) / 2 * 256 + D; }
 
+// Upper-triangle tile t (row-major over (bi, bj), bi <= bj) of an NB x NB
+// grid of 16-wide dim blocks: its row block bi and column block bj.
+constexpr int tile_bi(int t, int NB) {
+  int bi = 0;
+  while (bi < NB && t >= NB - bi) {
+    t -= NB - bi;
+    ++bi;
+  }
+  return bi < NB ? bi : 0;
+}
+constexpr int tile_bj(int t, int NB) {
+  int bi = 0;
+  while (bi < NB && t >= NB - bi) {
+    t -= NB - bi;
+    ++bi;
+  }
+  return bi < NB ? bi + t : 0;
+}
+
 struct WsLayout {
   size_t levels, nodes, units, mchunks, pchunks, part, ured, nodem, mu, dir, proj, tmp, wscale, total;
 };
@@ -450,22 +469,11 @@ __global__ __launch_bounds__(256, 2) void moment_kernel(PddpArgs a) {
   }
   double sx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   // wave w owns the upper-triangle tiles t = 4k + w (t enumerates (bi, bj),
-  // bi <= bj, row-major); acc[k] accumulates tile 4k + w, whose operands
-  // start at columns ao[k] = 16 bi and bo[k] = 16 bj (wave-uniform, so the
-  // MFMA loop has no branches and fixed accumulators)
+  // bi <= bj, row-major); acc[k] accumulates tile 4k + w (fixed
+  // accumulators, no branches in the MFMA loop)
   f64x4 acc[TPW];
-  int ao[TPW], bo[TPW];
 #pragma unroll
-  for (int k = 0; k < TPW; ++k) {
-    acc[k] = f64x4{0, 0, 0, 0};
-    int rem = 4 * k + wave, bi = 0;
-    while (bi < NB && rem >= NB - bi) {
-      rem -= NB - bi;
-      ++bi;
-    }
-    ao[k] = 16 * (bi < NB ? bi : 0);
-    bo[k] = 16 * (bi < NB ? bi + rem : 0);
-  }
+  for (int k = 0; k < TPW; ++k) acc[k] = f64x4{0, 0, 0, 0};
 
   u32x4 pre[RPT];
   bool ok[RPT];
@@ -498,19 +506,32 @@ __global__ __launch_bounds__(256, 2) void moment_kernel(PddpArgs a) {
     __syncthreads();
     if (base + SUB < len) fetch(base + SUB);
     const int steps = (len - base) < SUB ? ((len - base + 3) / 4) : SUB / 4;
-    for (int s = 0; s < steps; ++s) {
-      const double *xr = X + (4 * s + (lane >> 4)) * XS + (lane & 15);
-      double fa[TPW], fb[TPW];  // every operand of the step in flight at once
+    // A tile's A operand (dims 16 bi.., 4 tokens) and B operand (dims
+    // 16 bj..) are the same lane values as the one-block operand of block
+    // bi or bj: lane l holds x[token l / 16][16 b + l % 16]. So a step reads
+    // the NB blocks once and each of the wave's tiles takes two of them. The
+    // wave's tile list is made static per wave (a uniform switch), so the
+    // operands are fixed registers.
+    auto run = [&](auto wtag) {
+      constexpr int W = decltype(wtag)::value;
+      for (int s = 0; s < steps; ++s) {
+        const double *xr = X + (4 * s + (lane >> 4)) * XS + (lane & 15);
+        double v[NB];
 #pragma unroll
-      for (int k = 0; k < TPW; ++k) {
-        fa[k] = xr[ao[k]];
-        fb[k] = xr[bo[k]];
-      }
+        for (int bk = 0; bk < NB; ++bk) v[bk] = xr[16 * bk];
 #pragma unroll
-      for (int k = 0; k < TPW; ++k) {
-        if (4 * k + 3 < NT || 4 * k + wave < NT)
-          acc[k] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[k], fb[k], acc[k], 0, 0, 0);
+        for (int k = 0; k < TPW; ++k) {
+          if (4 * k + W < NT)
+            acc[k] = __builtin_amdgcn_mfma_f64_16x16x4f64(v[tile_bi(4 * k + W, NB)], v[tile_bj(4 * k + W, NB)],
+                                                          acc[k], 0, 0, 0);
+        }
       }
+    };
+    switch (wave) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      default: run(std::integral_constant<int, 3>{}); break;
     }
     __syncthreads();
   }
