@@ -582,6 +582,33 @@ __global__ __launch_bounds__(256) void reduce_kernel(PddpArgs a) {
 }
 
 // ---- node direction: grid (nnodes, BH), 256 threads -------------------------
+// A double moved across lanes by a DPP pattern (two 32-bit halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long bits = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)bits, CTRL, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(unsigned)(bits >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const unsigned long long bits = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)bits, l);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(bits >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+// Sum over the 64 lanes of a wave, returned to every lane: the quads by two
+// DPP quad permutes, the 16-lane rows by two DPP rotations (VALU steps, no
+// LDS round trip like a shuffle's), then the rows' sums read from lanes 0,
+// 16, 32 and 48 and added in a fixed order, so every lane and wave of equal
+// data gets the same bits.
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  x += dpp_f64<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f64<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f64<0x124>(x);  // row_ror:4
+  x += dpp_f64<0x128>(x);  // row_ror:8
+  return (readlane_f64(x, 0) + readlane_f64(x, 16)) + (readlane_f64(x, 32) + readlane_f64(x, 48));
+}
+
 // (value, index) max over a wave, lowest index among equal values
 __device__ __forceinline__ void wave_argmax(double &v, int &j) {
 #pragma unroll
@@ -765,21 +792,19 @@ __global__ __launch_bounds__(256) void power_kernel(PddpArgs a) {
     }
     wpart[part][col] = s0 + s1;
     __syncthreads();
-    // every wave forms all of w and its norm (entry lane + 64 q in lane
-    // order, the same sums in the same order in every wave), so no second
-    // exchange is needed; wave 0 writes the new u
-    double wq[(D + 63) / 64], nrm2 = 0.0;
+    // every wave forms all of w and its norm (entries lane + 64 q; the
+    // same sums in the same order in every wave), so no second exchange is
+    // needed; wave 0 writes the new u
+    double wq[(D + 63) / 64], sq = 0.0;
 #pragma unroll
     for (int q = 0; q < (D + 63) / 64; ++q) {
       double w = 0.0;
 #pragma unroll
       for (int p = 0; p < PARTS; ++p) w += wpart[p][lane + 64 * q];
       wq[q] = w;
-      double sq = w * w;
-#pragma unroll
-      for (int s = 32; s > 0; s >>= 1) sq += __shfl_xor(sq, s);
-      nrm2 += sq;
+      sq += w * w;
     }
+    const double nrm2 = wave_sum_f64(sq);
     if (nrm2 == 0.0) {  // all queries equal: every projection will be 0
       if (wave == 0) {
 #pragma unroll
