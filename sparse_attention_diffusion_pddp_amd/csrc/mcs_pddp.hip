@@ -889,8 +889,19 @@ __global__ __launch_bounds__(256) void project_kernel(PddpArgs a) {
         p += ((double)bf16_to_f32(v[u][m] & 0xffffu) - m8[2 * m]) * u8[2 * m];
         p += ((double)bf16_to_f32(v[u][m] >> 16) - m8[2 * m + 1]) * u8[2 * m + 1];
       }
-#pragma unroll
-      for (int s = LPT / 2; s > 0; s >>= 1) p += __shfl_xor(p, s);
+      // the sum over the token's LPT lanes on DPP, each a VALU step instead
+      // of a shuffle through LDS: LPT = 16 (a whole 16-lane row) rotates the
+      // row by 8 and by 4; LPT = 8 (half a row) mirrors each half. Then the
+      // two quad permutes. The lane with sub == 0, the only one that stores,
+      // adds in a fixed order.
+      if (LPT == 16) {
+        p += dpp_f64<0x128>(p);  // row_ror:8
+        p += dpp_f64<0x124>(p);  // row_ror:4
+      } else {
+        p += dpp_f64<0x141>(p);  // row_half_mirror: lane i and 7 - i of each 8
+      }
+      p += dpp_f64<0x4E>(p);  // quad_perm [2,3,0,1]
+      p += dpp_f64<0xB1>(p);  // quad_perm [1,0,3,2]
       if (i < c.len && sub == 0) {
         proj[c.off + i] = p;
         tmp[c.off + i] = tk[u];
