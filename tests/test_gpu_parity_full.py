@@ -1,6 +1,7 @@
 """GPU parity at the workloads' full sizes and launch configuration.
 
-Four layer shapes, each with all heads, d = 128, groups of 128:
+Four layer shapes, each with all heads, d = 128, groups of 128 (and the
+first also in groups of 64):
   * wan480p: 12 heads, N = 32760 (21x30x52 grid, last group 120 rows),
     K = 4914 (15%), plus one drifted reuse step; and the same layer at
     25% (K = 8190), the config's second density;
@@ -21,6 +22,7 @@ oracle then checks:
     every index row is ascending, unique and in range, and each group's
     probability mass sums to its row count.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -35,11 +37,13 @@ from tests import parity_util as U
 pytestmark = pytest.mark.gpu
 
 # case: (workload, density override or None, sampled heads, sampled groups;
-# -1 = the last, possibly short, group)
+# -1 = the last, possibly short, group[, group size override])
 SAMPLES = {
     "wan480p": ("wan480p", None, (0, 7), (0, 101, -1)),
     # the same layer at the config's second density (K = 8190)
     "wan480p@25": ("wan480p", 25, (3, 11), (0, 160, -1)),
+    # the same layer in 64-row groups (the 2-wave kernels, 512 groups a head)
+    "wan480p@T64": ("wan480p", None, (5,), (0, 333, -1), 64),
     "wan720p": ("wan720p", None, (0, 29), (0, 300, -1)),
     "longvideo": ("longvideo", None, (0, 17), (0, 500, -1)),
     "voxel3d": ("voxel3d", None, (0, 11), (0, 250, -1)),
@@ -49,10 +53,12 @@ SAMPLES = {
 @pytest.fixture(scope="module", params=list(SAMPLES))
 def run(request, lib):
     name = request.param
-    wname, pct, HEADS, GROUPS = SAMPLES[name]
+    wname, pct, HEADS, GROUPS = SAMPLES[name][:4]
     w = synth.WORKLOADS[wname]
     if pct is not None:
         w = w.with_density(pct)
+    if len(SAMPLES[name]) > 4:
+        w = dataclasses.replace(w, group_size=SAMPLES[name][4])
     B, H, N, d, T, K, G = w.batch, w.heads, w.seqlen, w.head_dim, w.group_size, w.topk, w.groups
     GROUPS = tuple(g % G for g in GROUPS)
     print(f"\n[{name} full size: H={H} N={N} d={d} T={T} K={K}]", flush=True)
