@@ -61,6 +61,8 @@ __global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_
   __shared__ __attribute__((aligned(1024))) bf16_t st0[2 * C::TILEB / 2];
   __shared__ __attribute__((aligned(1024))) bf16_t st1[2 * C::TILEB / 2];
   __shared__ __attribute__((aligned(16))) uint32_t idx_s[2][C::KT];  // key rows of upcoming tiles
+  // group modes: the group's row tokens, for the DMA of R (O_dense) rows
+  __shared__ int32_t tok_s[MODE == kModeDense ? 1 : C::TQ];
 
   const int nblocks = gridDim.x;
   const int work = xcd_remap(blockIdx.x, nblocks);
@@ -95,6 +97,7 @@ __global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_
     const int32_t *pr = a.perm + (int64_t)bh * a.N;
     token = pr[row_valid ? my_pos : row0];
   }
+  if (MODE != kModeDense && hh == 0) tok_s[rloc] = token;
   bf16x8 qf[D / 16];
   {
     const bf16_t *qrow = qb + (int64_t)token * a.sn + 8 * hh;
@@ -143,6 +146,32 @@ __global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+  const bool has_aux = (MODE == kModeResidual) || (MODE == kModeSparse && a.aux != nullptr);
+  u32x2 aux[D / 32][4];
+  // DMA of the group's R (O_dense) rows into a stage: row r = slot / CH at
+  // chunk (slot % CH) ^ swz(r), as the K rows; rows past the group take
+  // the first row's token (loaded, never used)
+  auto issue_aux = [&](bf16_t *stage) {
+    const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(a.aux + head_off, extent);
+    constexpr int LPA = C::TQ * C::ROWB / 1024 / NW;  // 1 KB loads per wave
+#pragma unroll
+    for (int i = 0; i < LPA; ++i) {
+      const int slot = (wave * LPA + i) * 64 + lane;
+      const int row = slot / C::CH;
+      const int chunk = (slot % C::CH) ^ swz<C::CH>(row);
+      const uint32_t off = (uint32_t)tok_s[row] * row_bytes + chunk * 16;
+      buffer_load_lds16(ra, (char *)stage + (wave * LPA + i) * 1024, off);
+    }
+  };
+  auto read_aux = [&](const bf16_t *stage) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int c = 4 * db + qd;
+        aux[db][qd] = *(const u32x2 *)((const char *)stage + rloc * C::ROWB + ((c ^ swz<C::CH>(rloc)) << 4) + 8 * hh);
+      }
+  };
   float m_run = kNegBig;  // running max, log2 units
   // running row sum, compensated (Kahan): over tens of thousands of keys
   // the mass of the many small probabilities would otherwise fall below
@@ -236,8 +265,10 @@ __global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_
       qkh(0);
       // the next tile's DMA (rows from idx_s[(t+1)&1]) goes out once the
       // first half's K reads are issued: its LDS writes then do not compete
-      // with them (2% faster than issuing it first)
+      // with them (2% faster than issuing it first); in the last tile the
+      // free stage takes the group's R rows instead
       if (!LAST) issue(t + 1, nxt);
+      if (LAST && MODE != kModeDense && has_aux) issue_aux(nxt);
       rescale(0);
       qkh(1);
       exps(0, pfa);
@@ -270,6 +301,10 @@ __global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_
       // this wave's DMA into `nxt` has landed (vmcnt(0)); then every wave's
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
+    } else if (MODE != kModeDense && has_aux) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      read_aux(nxt);
     }
   };
 
@@ -305,17 +340,7 @@ __global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_
   const float inv = 1.0f / l_run;
   const int64_t row_off = head_off + (int64_t)token * a.sn;
   bf16_t *orow = a.out + row_off;
-  // all of this lane's R / O_dense values are loaded before any store: out
-  // and aux may not be assumed disjoint by the compiler, which would
-  // otherwise serialise each load behind the previous store
-  u32x2 aux[D / 32][4];
-  const bool has_aux = (MODE == kModeResidual) || (MODE == kModeSparse && a.aux != nullptr);
-  if (has_aux) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) aux[db][qd] = *(const u32x2 *)(a.aux + row_off + 32 * db + 8 * qd + 4 * hh);
-  }
+  // group modes: R / O_dense came through LDS in the last tile
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
