@@ -36,11 +36,38 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_apply_wan480p_traffic.json
 KERNEL_SOURCES = ["mcs_attention.hip", "mcs_common.hpp", "mcs_lds.hpp"]
 
 
+def strip_comments(src: str) -> str:
+    """C++ source without its comments and with runs of whitespace made one
+    space, so that edits to comments alone keep the hash; string and
+    character literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_hash() -> str:
+    """Hash of the sparse-apply kernel's code (comments left out)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "sparse_attention_diffusion_pddp_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_attention_diffusion_pddp_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

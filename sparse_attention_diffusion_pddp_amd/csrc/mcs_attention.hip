@@ -14,6 +14,9 @@
 //                                            accumulator layout, no shuffle;
 //                                            V^T through transposing LDS reads.
 // Online softmax in base 2 (scale * log2 e folded in), fp32 statistics.
+// The group modes' R (or O_dense) rows reach LDS by DMA during the last key
+// tile, into the stage that tile leaves free, and the epilogue reads them
+// from there in the accumulator layout.
 //
 // MFMA operand layout used (32x32x16): lane l holds row/col (l % 32) and the
 // 8 reduction elements of half h = l / 32; accumulator value v of lane l is
@@ -44,7 +47,7 @@ struct AttnCfg {
 constexpr float kRescaleLog2 = 8.0f;
 
 // Waves per SIMD the LDS allows: one 8-wave (dense, 256-row) workgroup per
-// CU; two 4-wave ones (64.5 KB each); two 2-wave ones for 64-row groups,
+// CU; two 4-wave ones (65 KB each); two 2-wave ones for 64-row groups,
 // whose two 32 KB stages cap them at two per CU as well (one wave per SIMD).
 template <int NW>
 constexpr int attn_waves_per_simd() { return NW == 4 ? 2 : 1; }

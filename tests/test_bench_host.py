@@ -60,6 +60,18 @@ def test_committed_traffic_is_ignored_once_the_kernel_changes(monkeypatch):
     assert bench.load_traffic(989077340160) is None
 
 
+def test_kernel_hash_ignores_comments_only():
+    """Comments and layout do not count as a kernel change; code, strings
+    holding comment markers, and character literals do."""
+    a = "int f(int x) {\n  return x + 1;  // one more\n}\n"
+    b = "/* header */\nint f(int x) {\n    return x + 1;\n}  // end\n"
+    c = "int f(int x) {\n  return x + 2;\n}\n"
+    assert bench.strip_comments(a) == bench.strip_comments(b) == "int f(int x) { return x + 1; }"
+    assert bench.strip_comments(a) != bench.strip_comments(c)
+    s = 'const char *p = "a // b /* c */"; char q = \'"\'; // x'
+    assert bench.strip_comments(s) == 'const char *p = "a // b /* c */"; char q = \'"\';'
+
+
 @pytest.mark.parametrize("anchors,expect", [
     ((1,), {1: 0, 2: 1, 12: 1}),
     ((10, 26), {1: 0, 10: 0, 11: 1, 25: 1, 26: 2, 27: 3, 50: 3}),
