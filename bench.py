@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -71,16 +72,19 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(per_launch_flops):
+def load_traffic(per_launch_flops, head_dim, group_size):
     """HBM bytes per sparse_apply launch from committed rocprofv3 counters,
-    if they were taken on the current kernel source and on a launch of the
-    same work (the counted workload's effective FLOPs)."""
+    if they were taken on the current kernel source, on the same kernel
+    instance (head dim and group size) and on a launch of the same work (the
+    counted workload's effective FLOPs)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_hash") != kernel_hash() or t.get("per_launch_flop") != per_launch_flops:
+        return None
+    if t.get("head_dim") != head_dim or t.get("group_size") != group_size:
         return None
     return t.get("bytes_per_launch")
 
@@ -117,7 +121,11 @@ def write_traffic(fetch_dir, write_dir, fetch_copy_dir, write_copy_dir, kernel="
     fs, ws = copy_kib / fetch_c, copy_kib / write_c
     from sparse_attention_diffusion_pddp_amd import metrics, synth
     w = synth.WORKLOADS["wan480p"]  # the workload of the counted bench runs
+    m = re.match(r"attention_kernel<(\d+), (\d+), 1>", kernel)
+    if not m:
+        raise SystemExit(f"not a sparse-apply kernel instance: {kernel!r}")
     out = {"kernel": f"{kernel} (mcs_sparse_apply), wan480p 15%", "kernel_hash": kernel_hash(),
+           "head_dim": int(m.group(1)), "group_size": 32 * int(m.group(2)),
            "workload": "wan480p", "per_launch_flop": metrics.sparse_flops(w.batch, w.heads, w.seqlen, w.topk, w.head_dim),
            "dispatches": {"fetch": n_f, "write": n_w},
            "fetch_kib_per_launch": round(fetch, 1), "write_kib_per_launch": round(write, 1),
@@ -606,7 +614,7 @@ def main():
     rho, eta = metrics.kernel_speedup(dense_ms, reuse_ms, density)
     anchor_only = stage_ms["select_topk"] + stage_ms["residual"] + stage_ms["pddp"]
 
-    traffic = load_traffic(flops)
+    traffic = load_traffic(flops, d, T)
     achieved = value
     gemm = gemm_reference()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

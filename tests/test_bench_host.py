@@ -51,13 +51,17 @@ def test_write_traffic_scales_by_the_copy(tmp_path, monkeypatch):
     assert t["kernel_hash"] == bench.kernel_hash()
     # reported only for a launch of the counted work (wan480p at 15%)
     assert t["workload"] == "wan480p" and t["per_launch_flop"] == 989077340160
-    assert bench.load_traffic(989077340160) == (2000 * 2 + 500) * 1024
-    assert bench.load_traffic(17812571553792) is None  # longvideo's reuse call
+    assert t["head_dim"] == 128 and t["group_size"] == 128
+    assert bench.load_traffic(989077340160, 128, 128) == (2000 * 2 + 500) * 1024
+    assert bench.load_traffic(17812571553792, 128, 128) is None  # longvideo's reuse call
+    # the same work in 64-row groups runs another kernel instance
+    assert bench.load_traffic(989077340160, 128, 64) is None
 
 
 def test_committed_traffic_is_ignored_once_the_kernel_changes(monkeypatch):
+    assert bench.load_traffic(989077340160, 128, 128) is not None
     monkeypatch.setattr(bench, "kernel_hash", lambda: "not-the-hash")
-    assert bench.load_traffic(989077340160) is None
+    assert bench.load_traffic(989077340160, 128, 128) is None
 
 
 def test_kernel_hash_ignores_comments_only():
