@@ -5,10 +5,11 @@
 // One workgroup owns one tile of query rows: a PDDP query group (sparse,
 // residual) or a run of 256 consecutive tokens (dense: eight waves share each
 // K/V tile). Each of its waves owns 32 query rows. The key loop walks 64-key
-// tiles (128-key tiles on the dense path); a tile's K rows and V rows are
-// gathered by index (or read contiguously, dense) with LDS-DMA buffer loads
-// straight into one of two LDS stages (the next tile fills one stage while
-// the current one is consumed), and consumed by v_mfma_f32_32x32x16_bf16:
+// tiles (128-key tiles on the dense path, 32-key tiles for 64-row groups);
+// a tile's K rows and V rows are gathered by index (or read contiguously,
+// dense) with LDS-DMA buffer loads straight into one of two LDS stages (the
+// next tile fills one stage while the current one is consumed), and consumed
+// by v_mfma_f32_32x32x16_bf16:
 //   S^T (keys x queries) = K . Q^T        -- D/16 MFMAs per 32-key block
 //   O^T (dims x queries) += V^T . P^T     -- P^T comes straight from S^T's
 //                                            accumulator layout, no shuffle;
@@ -46,19 +47,25 @@ struct AttnCfg {
 // exponentials may reach 2^8, which fp32 and bf16 hold exactly as well as 1.
 constexpr float kRescaleLog2 = 8.0f;
 
+// Keys per tile: 128 on the 256-row dense path, 32 for the 2-wave (64-row)
+// group modes, 64 elsewhere.
+template <int NW, int MODE>
+constexpr int attn_key_tile() { return MODE == kModeDense && NW >= 8 ? 128 : (MODE != kModeDense && NW == 2 ? 32 : 64); }
+
 // Waves per SIMD the LDS allows: one 8-wave (dense, 256-row) workgroup per
-// CU; two 4-wave ones (65 KB each); two 2-wave ones for 64-row groups,
-// whose two 32 KB stages cap them at two per CU as well (one wave per SIMD).
-template <int NW>
-constexpr int attn_waves_per_simd() { return NW == 4 ? 2 : 1; }
+// CU; two 4-wave ones (65 KB each); four 2-wave ones for 64-row groups
+// (33 KB each: two 16 KB stages of 32-key tiles); two per CU for the 2-wave
+// dense form (32 KB stages), one wave per SIMD.
+template <int NW, int MODE>
+constexpr int attn_waves_per_simd() { return NW == 4 || (NW == 2 && MODE != kModeDense) ? 2 : 1; }
 
 template <int D, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, (attn_waves_per_simd<NW, MODE>())) void attention_kernel(AttnArgs a) {
   // 128-key tiles on the 256-row dense path (one barrier and DMA wait per
   // 128 keys; its single workgroup per CU has the LDS for them), 64 keys
   // elsewhere
-  using C = AttnCfg<D, NW, (MODE == kModeDense && NW >= 8) ? 128 : 64>;
-  static_assert(MODE == kModeDense || C::KT == 64, "one index per lane of wave 0 covers a tile");
+  using C = AttnCfg<D, NW, attn_key_tile<NW, MODE>()>;
+  static_assert(MODE == kModeDense || C::KT <= 64, "one index per lane of wave 0 covers a tile");
   // two pipeline stages as separate LDS objects, so the compiler can tell
   // the stage being filled by DMA from the one being read
   __shared__ __attribute__((aligned(1024))) bf16_t st0[2 * C::TILEB / 2];
@@ -123,12 +130,12 @@ __global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_
     }
     return idx_s[t & 1][j];
   };
-  auto fetch_idx = [&](int t) {  // wave 0 lane l: index of key t*KT + l
-    if (MODE != kModeDense && wave == 0)
+  auto fetch_idx = [&](int t) {  // wave 0 lane l < KT: index of key t*KT + l
+    if (MODE != kModeDense && wave == 0 && lane < C::KT)
       next_idx = __builtin_amdgcn_raw_buffer_load_b32(ri, (t * C::KT + lane) * 4, 0, 0);
   };
   auto store_idx = [&](int t) {
-    if (MODE != kModeDense && wave == 0) idx_s[t & 1][lane] = next_idx;
+    if (MODE != kModeDense && wave == 0 && lane < C::KT) idx_s[t & 1][lane] = next_idx;
   };
   // DMA tile t's K and V rows into a stage: wave w fills LDS slots
   // [(w*LPW + i)*64, +64) of 16 bytes; slot S is row S/CH, stored chunk S%CH,
@@ -184,7 +191,7 @@ __global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_
   const float c2 = a.scale_log2;
   const bool ragged = (nkeys % C::KT) != 0;
 
-  // one 64-key tile on `cur` while `nxt` fills with tile t+1:
+  // one key tile on `cur` while `nxt` fills with tile t+1:
   // S^T = K Q^T, online softmax, O^T += V^T P^T
   auto tile = [&](int t, const bf16_t *cur, bf16_t *nxt, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
@@ -263,7 +270,19 @@ __global__ __launch_bounds__(64 * NW, attn_waves_per_simd<NW>()) void attention_
         }
       }
     };
-    if constexpr (C::KT == 64) {
+    if constexpr (C::KT == 32) {
+      // 64-row groups: one 32-key half per tile, so that four 2-wave
+      // workgroups (two waves per SIMD) fit a CU's LDS; 16-21% faster than
+      // 64-key tiles at one wave per SIMD, outputs bitwise equal (the same
+      // halves in the same order)
+      bf16x8 pfa[2];
+      qkh(0);
+      if (!LAST) issue(t + 1, nxt);
+      if (LAST && MODE != kModeDense && has_aux) issue_aux(nxt);
+      rescale(0);
+      exps(0, pfa);
+      pvh(0, pfa);
+    } else if constexpr (C::KT == 64) {
       bf16x8 pfa[2], pfb[2];
       qkh(0);
       // the next tile's DMA (rows from idx_s[(t+1)&1]) goes out once the
