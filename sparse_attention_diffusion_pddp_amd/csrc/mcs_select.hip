@@ -45,8 +45,10 @@ struct MassCfg {
 // and at 128 VGPRs two such workgroups fill a CU (four waves per SIMD):
 // select 4.6% faster than one group per workgroup at the same occupancy,
 // identical indices (randomised-order A/B in one process); four groups per
-// workgroup (one per CU) were 1.9% slower than one. 64-row groups keep one
-// 2-wave group per workgroup, four per CU (two waves per SIMD).
+// workgroup (one per CU) were 1.9% slower than one. 64-row groups run four
+// to a workgroup, the same eight waves and 256 rows per K tile: select 5.04
+// -> 3.80 ms at wan480p with T = 64 against one 2-wave group per workgroup,
+// identical indices and masses.
 template <int D, int WPG, int GPW>
 __global__ __launch_bounds__(64 * WPG * GPW, WPG * GPW >= 4 ? 4 : 2) void mass_kernel(SelectArgs a) {
   constexpr int NW = WPG * GPW;
@@ -550,9 +552,9 @@ hipError_t launch_select(int head_dim, const SelectArgs &a, hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
   hipError_t e;
   if (head_dim == 128 && a.T == 128) e = launch_mass<128, 4, 2>(a, s);
-  else if (head_dim == 128 && a.T == 64) e = launch_mass<128, 2, 1>(a, s);
+  else if (head_dim == 128 && a.T == 64) e = launch_mass<128, 2, 4>(a, s);
   else if (head_dim == 64 && a.T == 128) e = launch_mass<64, 4, 2>(a, s);
-  else if (head_dim == 64 && a.T == 64) e = launch_mass<64, 2, 1>(a, s);
+  else if (head_dim == 64 && a.T == 64) e = launch_mass<64, 2, 4>(a, s);
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
   return launch_topk(a, s);
