@@ -1,8 +1,9 @@
 """GPU edge cases through the C-ABI, each against the oracle or a fixed fact:
 full density (sparse == dense, R at the rounding of O), a single selected
-key, one group shorter than the tile, N = 1, N = T + 1, all-equal queries,
-tied keys, batch > 1 with a strided (packed QKV) layout, bitwise run-to-run
-determinism, the error path, and the offload cache's bitwise round trip."""
+key and short sequences (N = 1, one group shorter than the tile, N = T + 1)
+in 128- and 64-row groups, all-equal queries, tied keys, batch > 1 with a
+strided (packed QKV) layout, bitwise run-to-run determinism, the error path,
+and the offload cache's bitwise round trip."""
 import math
 
 import numpy as np
@@ -118,25 +119,27 @@ def test_full_density_sparse_equals_dense(lib, N, T, d, pct):
     compare(g, oracle_head(head(q), head(k), head(v), T, K), 0, 0, K, N, "K=N")
 
 
-def test_single_key(lib):
-    w = synth.small_workload(500, heads=2, head_dim=128, group_size=128, density_pct=1)
+@pytest.mark.parametrize("T", [128, 64])
+def test_single_key(lib, T):
+    w = synth.small_workload(500, heads=2, head_dim=128, group_size=T, density_pct=1)
     q, k, v = synth.make_qkv(w, seed=12)
     K = 1
     qt, kt, vt = synth.drift_qkv(w, (q, k, v), step=1, seed=12)
-    g = pipeline(*(x.cuda() for x in (q, k, v)), 128, K, *(x.cuda() for x in (qt, kt, vt)))
+    g = pipeline(*(x.cuda() for x in (q, k, v)), T, K, *(x.cuda() for x in (qt, kt, vt)))
     for h in range(2):
-        orc = oracle_head(head(q, 0, h), head(k, 0, h), head(v, 0, h), 128, K,
+        orc = oracle_head(head(q, 0, h), head(k, 0, h), head(v, 0, h), T, K,
                           head(qt, 0, h), head(kt, 0, h), head(vt, 0, h))
-        compare(g, orc, 0, h, K, 500, f"K=1 h{h}")
+        compare(g, orc, 0, h, K, 500, f"K=1 T={T} h{h}")
 
 
+@pytest.mark.parametrize("T", [128, 64])
 @pytest.mark.parametrize("N", [1, 37, 100, 128, 129])
-def test_short_sequences(lib, N):
-    w = synth.small_workload(N, heads=1, head_dim=128, group_size=128, density_pct=30)
+def test_short_sequences(lib, N, T):
+    w = synth.small_workload(N, heads=1, head_dim=128, group_size=T, density_pct=30)
     q, k, v = synth.make_qkv(w, seed=13)
     K = w.topk
-    g = pipeline(*(x.cuda() for x in (q, k, v)), 128, K)
-    compare(g, oracle_head(head(q), head(k), head(v), 128, K), 0, 0, K, N, f"N={N}")
+    g = pipeline(*(x.cuda() for x in (q, k, v)), T, K)
+    compare(g, oracle_head(head(q), head(k), head(v), T, K), 0, 0, K, N, f"N={N} T={T}")
     if N == 1:
         assert np.array_equal(g["o"][0, 0, 0], v[0, 0, 0].float().numpy())
 
