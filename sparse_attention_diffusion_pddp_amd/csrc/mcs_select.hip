@@ -3,14 +3,15 @@
 // group, A[g][j] = sum_{i in g} P_ij, and the per-group top-K of single keys
 // (ties -> lower key index), stored ascending.
 //
-// mass_kernel: one workgroup per (b, h, g). Each wave holds 32 of the group's
-// query rows as MFMA A-operands; 64-key tiles of K arrive by LDS-DMA (16
-// bytes per lane straight into LDS, chunks XOR-swizzled per row) in two
-// stages, the next tile loading while the current one is used. S = Q . K^T
-// via v_mfma_f32_32x32x16_bf16 leaves every lane with 16 query rows of ONE
-// key, so the column sum over the wave is 16 local adds plus one
-// cross-half add; the 4 (or 2) waves' partial sums meet in LDS and are added
-// in a fixed order (no atomics).
+// mass_kernel / mass_wide_kernel: one workgroup per GPW groups of one head.
+// Each wave holds 32 (or, in the wide form, 64) of a group's query rows as
+// MFMA A-operands; K tiles arrive by LDS-DMA (16 bytes per lane straight
+// into LDS, chunks XOR-swizzled per row) in two stages, the next tile
+// loading while the current one is used. S = Q . K^T via
+// v_mfma_f32_32x32x16_bf16 leaves every lane with 16 query rows of ONE key,
+// so the column sum over 32 rows is 16 local adds plus one cross-half add;
+// the 32-row blocks' partial sums meet in LDS and are added in a fixed order
+// (no atomics), so both forms give the same bits.
 //
 // Top-K: one workgroup per (b, h, g). A radix select, most significant
 // digit first, finds the K-th largest mass; an ordered pass with ballot
@@ -30,10 +31,10 @@
 
 namespace mcs {
 
-template <int D, int NW>
+template <int D, int NW, int KT_ = 64>
 struct MassCfg {
   static constexpr int NT = 64 * NW;
-  static constexpr int KT = 64;                  // keys per tile
+  static constexpr int KT = KT_;                 // keys per tile
   static constexpr int CH = D / 8;               // 16-byte chunks per row
   static constexpr int TILEB = KT * D * 2;       // bytes of one K tile
   static constexpr int LPW = TILEB / 1024 / NW;  // 1 KB LDS-DMA loads per wave
@@ -53,6 +54,7 @@ template <int D, int WPG, int GPW>
 __global__ __launch_bounds__(64 * WPG * GPW, WPG * GPW >= 4 ? 4 : 2) void mass_kernel(SelectArgs a) {
   constexpr int NW = WPG * GPW;
   using C = MassCfg<D, NW>;
+  static_assert(C::NT >= GPW * C::KT, "one finishing thread per key of each group");
   // two stages as separate LDS objects, so the compiler can tell the stage
   // being filled by DMA from the one being read
   __shared__ __attribute__((aligned(1024))) bf16_t st0[C::KT * D];
@@ -153,6 +155,153 @@ __global__ __launch_bounds__(64 * WPG * GPW, WPG * GPW >= 4 ? 4 : 2) void mass_k
       float lo, hi;
       cross_half(cs, lo, hi);
       if (hh == 0) partial[t & 1][wave][r] = lo + hi;
+    }
+    // this wave's DMA into `nxt` has landed; then every wave's, and every
+    // wave's partial sums are in LDS
+    if (!LAST) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  };
+
+  issue(0, st0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    tile(t, st0, st1, std::false_type{});
+    tile(t + 1, st1, st0, std::false_type{});
+  }
+  if (ntiles - t == 2) {
+    tile(t, st0, st1, std::false_type{});
+    tile(t + 1, st1, st0, std::true_type{});
+  } else {
+    tile(t, st0, st1, std::true_type{});
+  }
+  finish(ntiles - 1);
+}
+
+// The same sweep with 64 query rows per wave (WPG waves per group, GPW
+// groups per workgroup, KT-key tiles): each K fragment read from LDS feeds
+// two MFMAs (rows 0-31 and 32-63 of the wave), at two waves per SIMD. For
+// 128-row groups at d = 128 it runs four groups per workgroup, eight waves
+// sharing each 128-key tile's DMA (512 rows), one workgroup per CU: select
+// 1.6-2.4% faster than two groups per workgroup of mass_kernel at wan480p
+// on three boxes (3% at longvideo with 64-key tiles), identical masses and
+// indices.
+template <int D, int WPG, int GPW, int KT>
+__global__ __launch_bounds__(64 * WPG * GPW, 2) void mass_wide_kernel(SelectArgs a) {
+  constexpr int NW = WPG * GPW;
+  using C = MassCfg<D, NW, KT>;
+  static_assert(C::NT >= GPW * C::KT, "one finishing thread per key of each group");
+  // two stages as separate LDS objects, so the compiler can tell the stage
+  // being filled by DMA from the one being read
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[C::KT * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[C::KT * D];
+  __shared__ float partial[2][2 * NW][C::KT];  // one row per 32-row half of a wave
+
+  const int sets = (a.G + GPW - 1) / GPW;  // workgroups per head
+  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = work / sets;
+  const int gs = work - bh * sets;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = wave % WPG;               // wave within its group
+  const int g = GPW * gs + wave / WPG;     // this wave's group (past G: none, rows masked)
+  const bool gvalid = g < a.G;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const bf16_t *qb = a.q + head_off;
+  const int32_t *pr = a.perm + (int64_t)bh * a.N;
+  const float *lse = a.lse + (int64_t)bh * a.N;
+  const int row0 = (gvalid ? g : 0) * a.T;
+  const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const uint32_t extent = (uint32_t)(a.N - 1) * row_bytes + D * 2;
+  const __amdgpu_buffer_rsrc_t rk = uniform_rsrc(a.k + head_off, extent);
+
+  // A-operand rows: query 64*wg + 32*m + l32 of the group
+  bf16x8 qf[2][D / 16];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int r = 64 * wg + 32 * m + l32;
+    const int pos = row0 + r;
+    const bool ok = r < a.T && pos < a.N;
+    const bf16_t *qrow = qb + (int64_t)pr[ok ? pos : row0] * a.sn + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[m][s] = *(const bf16x8 *)(qrow + 16 * s);
+  }
+  // accumulator rows held by this lane: 64*wg + 32*m + 8*(v/4) + 4*hh + (v%4)
+  float l2[2][16];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = 64 * wg + 32 * m + 8 * (v >> 2) + 4 * hh + (v & 3);
+      const int pos = row0 + r;
+      const bool ok = gvalid && r < a.T && pos < a.N;
+      l2[m][v] = ok ? lse[pr[pos]] * kLog2e : 1.0e30f;  // invalid row: P = 0
+    }
+  const float c2 = a.scale_log2;
+
+  const int ntiles = (a.N + C::KT - 1) / C::KT;
+  // DMA of tile t's K rows: slot S of the stage is row S / CH, stored chunk
+  // S % CH, holding logical chunk (S % CH) ^ swz(row); rows past N repeat
+  // the last key (their sums are not written)
+  auto issue = [&](int t, bf16_t *stage) {
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      const int slot = (wave * C::LPW + i) * 64 + lane;
+      const int row = slot / C::CH;
+      const int chunk = (slot % C::CH) ^ swz<C::CH>(row);
+      const int key = t * C::KT + row;
+      const uint32_t off = (uint32_t)(key < a.N ? key : a.N - 1) * row_bytes + chunk * 16;
+      buffer_load_lds16(rk, (char *)stage + (wave * C::LPW + i) * 1024, off);
+    }
+  };
+
+  // thread fg * KT + fk finishes key fk of the tile for group GPW*gs + fg
+  const int fg = tid / C::KT;
+  const int fk = tid - fg * C::KT;
+  const bool fval = fg < GPW && GPW * gs + fg < a.G;
+  float *mass_row = a.mass + ((int64_t)bh * a.G + (GPW * gs + fg)) * a.N;
+  auto finish = [&](int t) {  // tile t's column sums over the group's 32-row blocks, fixed order
+    if (fval) {
+      const int key = t * C::KT + fk;
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < 2 * WPG; ++w) s += partial[t & 1][2 * WPG * fg + w][fk];
+      if (key < a.N) mass_row[key] = s;
+    }
+  };
+  auto tile = [&](int t, const bf16_t *cur, bf16_t *nxt, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    if (t > 0) finish(t - 1);
+#pragma unroll
+    for (int kb = 0; kb < C::KT / 32; ++kb) {
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+      const int r = 32 * kb + l32;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const bf16x8 kf = *(const bf16x8 *)(cur + r * D + (((2 * s + hh) ^ swz<C::CH>(r)) << 3));
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf, s1, 0, 0, 0);
+      }
+      // the next tile's DMA once the first half's K reads are out, so its
+      // LDS writes do not compete with them
+      if (kb == 0 && !LAST) issue(t + 1, nxt);
+      float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) c0 += fast_exp2(__builtin_fmaf(s0[v], c2, -l2[0][v]));
+#pragma unroll
+      for (int v = 0; v < 16; ++v) c1 += fast_exp2(__builtin_fmaf(s1[v], c2, -l2[1][v]));
+      float lo0, hi0, lo1, hi1;
+      cross_half(c0, lo0, hi0);
+      cross_half(c1, lo1, hi1);
+      if (hh == 0) {
+        partial[t & 1][2 * wave][r] = lo0 + hi0;
+        partial[t & 1][2 * wave + 1][r] = lo1 + hi1;
+      }
     }
     // this wave's DMA into `nxt` has landed; then every wave's, and every
     // wave's partial sums are in LDS
@@ -526,6 +675,13 @@ __global__ __launch_bounds__(NTH) void topk_reg_kernel(SelectArgs a) {
   }
 }
 
+template <int D, int WPG, int GPW, int KT>
+static hipError_t launch_mass_wide(const SelectArgs &a, hipStream_t s) {
+  const int nblocks = a.B * a.H * ((a.G + GPW - 1) / GPW);
+  hipLaunchKernelGGL((mass_wide_kernel<D, WPG, GPW, KT>), dim3(nblocks), dim3(64 * WPG * GPW), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int WPG, int GPW>
 static hipError_t launch_mass(const SelectArgs &a, hipStream_t s) {
   const int nblocks = a.B * a.H * ((a.G + GPW - 1) / GPW);
@@ -551,7 +707,7 @@ hipError_t launch_select(int head_dim, const SelectArgs &a, hipStream_t s) {
   const int nblocks = a.B * a.H * a.G;
   if (nblocks <= 0) return hipSuccess;
   hipError_t e;
-  if (head_dim == 128 && a.T == 128) e = launch_mass<128, 4, 2>(a, s);
+  if (head_dim == 128 && a.T == 128) e = launch_mass_wide<128, 2, 4, 128>(a, s);
   else if (head_dim == 128 && a.T == 64) e = launch_mass<128, 2, 4>(a, s);
   else if (head_dim == 64 && a.T == 128) e = launch_mass<64, 4, 2>(a, s);
   else if (head_dim == 64 && a.T == 64) e = launch_mass<64, 2, 4>(a, s);
